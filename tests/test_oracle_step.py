@@ -1,0 +1,350 @@
+"""Pins for the oracle's decode step.
+
+Each test ties the oracle to something other than itself: exact rational
+arithmetic, the dense-matrix recurrence, closed-form invariants of the gated
+delta rule (the decay and key-direction correction channels described in
+"线性注意力状态量化难题" section 时间维度), or the quantizer's definition
+evaluated independently in numpy.  A plausible slip in the oracle -- a dropped
+term, a sign, a transposed operand, a wrong index -- fails at least one."""
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+
+
+def _unit(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _f32(x):
+    return np.asarray(x, np.float32)
+
+
+def _fp32_tile(orc, S):
+    dk, dv = S.shape
+    one_r, one_c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+    return orc.encode_tile(32, dk, dv, S, one_r, one_c), one_r, one_c
+
+
+# ------------------------------------------------------------ exact rational
+
+def test_one_step_matches_exact_rational_dense_form(orc):
+    """S' = alpha (I - beta k k^T) S + beta k v^T and o = S'^T q, evaluated with
+    Fractions on fp32-exact inputs, against the oracle's FP32-state step."""
+    rng = np.random.default_rng(1)
+    dk, dv = 4, 6  # non-square: a transposed operand cannot pass
+    S = _f32(rng.standard_normal((dk, dv)))
+    q, k = _f32(rng.standard_normal(dk)), _f32(rng.standard_normal(dk))
+    v = _f32(rng.standard_normal(dv))
+    alpha, beta = np.float32(0.8125), np.float32(0.375)
+    tile, r1, c1 = _fp32_tile(orc, S.astype(np.float64))
+    new_tile, o = orc.step_tile(32, dk, dv, tile, r1, c1, q, k, v, alpha, beta)
+    Sn = orc.decode_tile(32, dk, dv, new_tile, r1, c1)
+
+    Sf = [[F(float(S[i, j])) for j in range(dv)] for i in range(dk)]
+    kf, qf, vf = [F(float(x)) for x in k], [F(float(x)) for x in q], [F(float(x)) for x in v]
+    a, b = F(float(alpha)), F(float(beta))
+    A = [[a * ((1 if i == l else 0) - b * kf[i] * kf[l]) for l in range(dk)] for i in range(dk)]
+    Sx = [[sum(A[i][l] * Sf[l][j] for l in range(dk)) + b * kf[i] * vf[j] for j in range(dv)]
+          for i in range(dk)]
+    ox = [sum(qf[i] * Sx[i][j] for i in range(dk)) for j in range(dv)]
+    for i in range(dk):
+        for j in range(dv):
+            # stored state is the exact value rounded once to fp32
+            assert Sn[i, j] == float(np.float32(float(Sx[i][j])))
+    for j in range(dv):
+        assert abs(float(o[j]) - float(ox[j])) <= 2 ** -23 * abs(float(ox[j])) + 1e-30
+
+
+def test_bruteforce_matches_exact_rational(orc):
+    rng = np.random.default_rng(2)
+    dk, dv, T = 3, 5, 3
+    S0 = _f32(rng.standard_normal((dk, dv))).astype(np.float64)
+    q, k = _f32(rng.standard_normal((T, dk))), _f32(rng.standard_normal((T, dk)))
+    v = _f32(rng.standard_normal((T, dv)))
+    alpha = _f32(rng.uniform(0.5, 1, T))
+    beta = _f32(rng.uniform(0, 1, T))
+    ST, o = orc.bruteforce(S0, q, k, v, alpha, beta)
+    S = [[F(float(S0[i, j])) for j in range(dv)] for i in range(dk)]
+    for t in range(T):
+        kf = [F(float(x)) for x in k[t]]
+        a, b = F(float(alpha[t])), F(float(beta[t]))
+        u = [sum(kf[i] * S[i][j] for i in range(dk)) for j in range(dv)]
+        S = [[a * S[i][j] - a * b * kf[i] * u[j] + b * kf[i] * F(float(v[t, j])) for j in range(dv)]
+             for i in range(dk)]
+        ot = [sum(F(float(q[t, i])) * S[i][j] for i in range(dk)) for j in range(dv)]
+        np.testing.assert_allclose(o[t], [float(x) for x in ot], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ST, [[float(x) for x in row] for row in S], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ unrolled recurrence
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (8, 24)])
+def test_fp32_path_matches_bruteforce_recurrence(orc, dk, dv):
+    """FP32 state through T oracle steps vs the dense Phi-product recurrence."""
+    rng = np.random.default_rng(dk + dv)
+    T = 8
+    S0 = _f32(rng.normal(0, 0.1, (dk, dv))).astype(np.float64)
+    q, k = _f32(_unit(rng, T, dk)), _f32(_unit(rng, T, dk))
+    v = _f32(rng.standard_normal((T, dv)))
+    alpha = _f32(np.exp(-np.log1p(np.exp(rng.standard_normal(T)))))
+    beta = _f32(rng.uniform(0, 1, T))
+    ST, o_ref = orc.bruteforce(S0, q, k, v, alpha, beta)
+    tile, r1, c1 = _fp32_tile(orc, S0)
+    for t in range(T):
+        tile, o = orc.step_tile(32, dk, dv, tile, r1, c1, q[t], k[t], v[t], alpha[t], beta[t])
+        np.testing.assert_allclose(o, o_ref[t], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(orc.decode_tile(32, dk, dv, tile, r1, c1), ST, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------ closed-form invariants
+
+def _quant_tile(orc, rng, bits, dk, dv):
+    r = _f32(rng.uniform(0.5, 2.0, dk))
+    c = _f32(rng.uniform(0.01, 0.05, dv))
+    Q = 2 ** (bits - 1) - 1
+    codes = rng.integers(-Q, Q + 1, (dk, dv))
+    s = np.array([[orc.step_size(float(r[i]), float(c[j])) for j in range(dv)] for i in range(dk)])
+    return orc.encode_tile(bits, dk, dv, codes * s, r, c), r, c, codes, s
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_I1_pure_decay(orc, bits):
+    rng = np.random.default_rng(10 + bits)
+    dk, dv = 16, 32
+    tile, r, c, codes, s = _quant_tile(orc, rng, bits, dk, dv)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv))
+    # beta = 0, alpha = 1: codes unchanged, bit-exact, over several steps
+    t = tile
+    for _ in range(5):
+        t, o = orc.step_tile(bits, dk, dv, t, r, c, q, k, v, 1.0, 0.0)
+        assert np.array_equal(t, tile)
+        np.testing.assert_allclose(o, orc.readout_tile(bits, dk, dv, tile, r, c, q), rtol=0, atol=0)
+    # beta = 0, alpha < 1: q' = quant(alpha * S) elementwise (numpy model of the quantizer)
+    alpha = np.float32(0.7)
+    t, o = orc.step_tile(bits, dk, dv, tile, r, c, q, k, v, alpha, 0.0)
+    Q = 2 ** (bits - 1) - 1
+    z = (float(alpha) * codes * s / s).astype(np.float32).astype(np.float64)
+    want = np.clip(np.round(z), -Q, Q)  # numpy rounds half to even
+    got = orc.decode_tile(bits, dk, dv, t, r, c) / s
+    assert np.array_equal(np.round(got), want)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8, 16, 32])
+def test_I2_write_into_row(orc, bits):
+    """alpha = beta = 1, k = e_m: row m becomes v, every other row is untouched."""
+    rng = np.random.default_rng(20 + bits)
+    dk, dv, m = 16, 16, 5
+    if bits <= 8:
+        tile, r, c, codes, s = _quant_tile(orc, rng, bits, dk, dv)
+    else:
+        S = rng.standard_normal((dk, dv))
+        r, c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+        tile = orc.encode_tile(bits, dk, dv, S, r, c)
+        s = np.ones((dk, dv))
+    k = np.zeros(dk, np.float32)
+    k[m] = 1
+    q = _f32(rng.standard_normal(dk))
+    Q = 2 ** (bits - 1) - 1 if bits <= 8 else None
+    v = _f32(rng.uniform(-0.9, 0.9, dv) * (Q * s[m].min() if bits <= 8 else 3))
+    before = orc.decode_tile(bits, dk, dv, tile, r, c)
+    t, o = orc.step_tile(bits, dk, dv, tile, r, c, q, k, v, 1.0, 1.0)
+    after = orc.decode_tile(bits, dk, dv, t, r, c)
+    others = [i for i in range(dk) if i != m]
+    assert np.array_equal(after[others], before[others])
+    if bits <= 8:
+        want = np.clip(np.round((v.astype(np.float64) / s[m]).astype(np.float32)), -Q, Q)
+        assert np.array_equal(np.round(after[m] / s[m]), want)
+    elif bits == 16:
+        assert np.array_equal(after[m], v.astype(np.float16).astype(np.float64))
+    else:
+        assert np.array_equal(after[m], v.astype(np.float64))
+
+
+def test_I3_associative_recall_fp32(orc):
+    rng = np.random.default_rng(30)
+    dk, dv = 16, 12
+    K, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = K.T  # rows orthonormal
+    V = rng.standard_normal((dk, dv))
+    tile, r1, c1 = _fp32_tile(orc, np.zeros((dk, dv)))
+    for t in range(dk):
+        tile, _ = orc.step_tile(32, dk, dv, tile, r1, c1, np.zeros(dk), K[t], V[t], 1.0, 1.0)
+    S = orc.decode_tile(32, dk, dv, tile, r1, c1)
+    Kf = _f32(K).astype(np.float64)  # the step saw fp32 keys
+    for t in range(dk):
+        np.testing.assert_allclose(S.T @ Kf[t], V[t], rtol=1e-5, atol=2e-6)
+
+
+def test_I4_delta_identity_and_I5_norm_bound(orc):
+    rng = np.random.default_rng(40)
+    dk, dv = 16, 24
+    for trial in range(20):
+        S = rng.standard_normal((dk, dv))
+        k = _unit(rng, 1, dk)[0].astype(np.float64)
+        v = rng.standard_normal(dv)
+        alpha, beta = rng.uniform(0.05, 1.0), rng.uniform(0, 1)
+        tile, r1, c1 = _fp32_tile(orc, S)
+        S32 = orc.decode_tile(32, dk, dv, tile, r1, c1)
+        k32, v32 = _f32(k), _f32(v)
+        a32, b32 = np.float32(alpha), np.float32(beta)
+        t, _ = orc.step_tile(32, dk, dv, tile, r1, c1, np.zeros(dk), k32, v32, a32, b32)
+        Sn = orc.decode_tile(32, dk, dv, t, r1, c1)
+        kk = k32.astype(np.float64)
+        nk2 = kk @ kk
+        # k^T S' = alpha (1 - beta |k|^2) k^T S + beta |k|^2 v^T
+        lhs = kk @ Sn
+        rhs = float(a32) * (1 - float(b32) * nk2) * (kk @ S32) + float(b32) * nk2 * v32
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-5, atol=1e-5)
+        # |S'|_F <= alpha |S|_F + beta |k| |v|  (|k| = 1 up to fp32 rounding)
+        bound = float(a32) * np.linalg.norm(S32) + float(b32) * np.sqrt(nk2) * np.linalg.norm(v32)
+        assert np.linalg.norm(Sn) <= bound * (1 + 1e-6)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8, 16])
+def test_I7_readout_identity(orc, bits):
+    """o = S'^T q equals alpha S^T q + beta (q.k)(v - alpha u), u = S^T k."""
+    rng = np.random.default_rng(50 + bits)
+    dk, dv = 32, 16
+    if bits <= 8:
+        tile, r, c, codes, s = _quant_tile(orc, rng, bits, dk, dv)
+    else:
+        r, c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+        tile = orc.encode_tile(16, dk, dv, rng.standard_normal((dk, dv)), r, c)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv))
+    alpha, beta = np.float32(0.9), np.float32(0.6)
+    S = orc.decode_tile(bits, dk, dv, tile, r, c)
+    _, o = orc.step_tile(bits, dk, dv, tile, r, c, q, k, v, alpha, beta)
+    qd, kd, vd = q.astype(float), k.astype(float), v.astype(float)
+    u = S.T @ kd
+    want = float(alpha) * (S.T @ qd) + float(beta) * (qd @ kd) * (vd - float(alpha) * u)
+    np.testing.assert_allclose(o, want, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_I8_code_domain_requantization(orc, bits):
+    """New codes equal clamp(rne(alpha q + (beta k_i / r_i)(v_j - alpha u_j) / c_j)),
+    except where that value sits within 1e-6 of a rounding boundary."""
+    rng = np.random.default_rng(60 + bits)
+    dk, dv = 32, 32
+    Q = 2 ** (bits - 1) - 1
+    tile, r, c, codes, s = _quant_tile(orc, rng, bits, dk, dv)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv) * 0.3)
+    alpha, beta = np.float32(0.95), np.float32(0.5)
+    S = orc.decode_tile(bits, dk, dv, tile, r, c)
+    t, _ = orc.step_tile(bits, dk, dv, tile, r, c, q, k, v, alpha, beta)
+    new = np.round(orc.decode_tile(bits, dk, dv, t, r, c) / s).astype(int)
+    u = S.T @ k.astype(float)
+    a_i = float(beta) * k.astype(float) / r.astype(float)
+    b_j = (v.astype(float) - float(alpha) * u) / c.astype(float)
+    z = float(alpha) * codes + np.outer(a_i, b_j)
+    want = np.clip(np.round(z), -Q, Q).astype(int)
+    near = np.abs(np.abs(z - np.floor(z)) - 0.5) < 1e-6
+    assert np.array_equal(new[~near], want[~near])
+    assert (z.min() < -Q or z.max() > Q) or bits == 8  # the clamp is exercised for 4/6 bit
+
+
+def test_P3_pivot_is_fp16_of_fp32_path(orc):
+    rng = np.random.default_rng(70)
+    dk, dv = 16, 16
+    S = rng.standard_normal((dk, dv)).astype(np.float16).astype(np.float64)
+    r, c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+    t16 = orc.encode_tile(16, dk, dv, S, r, c)
+    t32 = orc.encode_tile(32, dk, dv, S, r, c)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv))
+    n16, o16 = orc.step_tile(16, dk, dv, t16, r, c, q, k, v, 0.9, 0.4)
+    n32, o32 = orc.step_tile(32, dk, dv, t32, r, c, q, k, v, 0.9, 0.4)
+    assert np.array_equal(o16, o32)
+    S32 = orc.decode_tile(32, dk, dv, n32, r, c)
+    assert np.array_equal(orc.decode_tile(16, dk, dv, n16, r, c),
+                          S32.astype(np.float16).astype(np.float64))
+
+
+def test_nonfinite_inputs_follow_the_stated_rule(orc):
+    rng = np.random.default_rng(80)
+    dk, dv = 16, 16
+    tile, r, c, codes, s = _quant_tile(orc, rng, 8, dk, dv)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv))
+    t, o = orc.step_tile(8, dk, dv, tile, r, c, q, k, v, np.nan, 0.5)
+    assert np.all(np.round(orc.decode_tile(8, dk, dv, t, r, c) / s) == 0)  # NaN -> code 0
+    assert np.all(np.isnan(o))
+    # out-of-range values saturate to +-Q by sign (a huge finite gate; an infinite
+    # one would make 0 * inf = NaN in the beta term)
+    t, o = orc.step_tile(8, dk, dv, tile, r, c, q, k, v, 1e30, 0.0)
+    got = np.round(orc.decode_tile(8, dk, dv, t, r, c) / s)
+    assert np.all(got[codes > 0] == 127) and np.all(got[codes < 0] == -127)
+    assert np.all(got[codes == 0] == 0)
+
+
+# ------------------------------------------------------------ pool level
+
+def test_pool_step_equals_per_tile_steps_with_slot_indirection(orc):
+    rng = np.random.default_rng(90)
+    dk = dv = 16
+    bits = np.array([8, 4, 16, 6, 32], np.uint8)
+    H = bits.size
+    off, slab = orc.pool_layout(bits, dk, dv)
+    n_slots = 5
+    pool = rng.integers(0, 256, n_slots * slab, dtype=np.uint8)
+    r = _f32(rng.uniform(0.5, 2, (H, dk)))
+    c = _f32(rng.uniform(0.01, 0.05, (H, dv)))
+    # make fp16/fp32 tiles hold finite values
+    for p in range(n_slots):
+        for h in (2, 4):
+            t = orc.encode_tile(int(bits[h]), dk, dv, rng.standard_normal((dk, dv)), r[h], c[h])
+            pool[p * slab + off[h]: p * slab + off[h] + t.size] = t
+    slots = np.array([3, 0, 4], np.int32)
+    n = slots.size
+    q, k = _f32(_unit(rng, n * H, dk)), _f32(_unit(rng, n * H, dk))
+    v = _f32(rng.standard_normal((n * H, dv)))
+    alpha, beta = _f32(rng.uniform(0.5, 1, n * H)), _f32(rng.uniform(0, 1, n * H))
+    ref = pool.copy()
+    o = orc.step_pool(pool, bits, dk, dv, r, c, slots, q, k, v, alpha, beta, n_threads=3)
+    for ni, p in enumerate(slots):
+        for h in range(H):
+            lo = p * slab + off[h]
+            tb = orc.tile_bytes(int(bits[h]), dk, dv)
+            t, oo = orc.step_tile(int(bits[h]), dk, dv, ref[lo:lo + tb], r[h], c[h], q[ni * H + h],
+                                  k[ni * H + h], v[ni * H + h], alpha[ni * H + h], beta[ni * H + h])
+            assert np.array_equal(pool[lo:lo + tb], t)
+            assert np.array_equal(o[ni, h], oo)
+    # slots not in the batch (1, 2) and tile padding are untouched
+    for p in (1, 2):
+        assert np.array_equal(pool[p * slab:(p + 1) * slab], ref[p * slab:(p + 1) * slab])
+    # empty batch is a no-op
+    before = pool.copy()
+    orc.step_pool(pool, bits, dk, dv, r, c, np.zeros(0, np.int32), np.zeros(0), np.zeros(0),
+                  np.zeros(0), np.zeros(0), np.zeros(0))
+    assert np.array_equal(pool, before)
+    # readout_pool is the non-mutating S^T q
+    o2 = orc.readout_pool(pool, bits, dk, dv, r, c, slots, q)
+    for ni, p in enumerate(slots):
+        for h in range(H):
+            lo = p * slab + off[h]
+            tb = orc.tile_bytes(int(bits[h]), dk, dv)
+            assert np.array_equal(o2[ni, h], orc.readout_tile(int(bits[h]), dk, dv, pool[lo:lo + tb],
+                                                               r[h], c[h], q[ni * H + h]))
+    assert np.array_equal(pool, before)
+
+
+def test_store_pool_matches_encode(orc):
+    rng = np.random.default_rng(91)
+    dk = dv = 16
+    bits = np.array([4, 6, 8, 16, 32], np.uint8)
+    H = bits.size
+    off, slab = orc.pool_layout(bits, dk, dv)
+    pool = np.zeros(2 * slab, np.uint8)
+    r = _f32(rng.uniform(0.5, 2, (H, dk)))
+    c = _f32(rng.uniform(0.01, 0.05, (H, dv)))
+    S = _f32(rng.normal(0, 1, (1, H, dk, dv)))
+    orc.store_pool(pool, bits, dk, dv, r, c, np.array([1], np.int32), S)
+    assert not pool[:slab].any()
+    for h in range(H):
+        t = orc.encode_tile(int(bits[h]), dk, dv, S[0, h].astype(np.float64), r[h], c[h])
+        assert np.array_equal(pool[slab + off[h]: slab + off[h] + t.size], t)
