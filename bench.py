@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the fused quantized gated delta-rule decode step on one MI355X.
+
+Workload: the STEPQuant pages' serving point -- 70 concurrent requests x 2304
+recurrent heads ("K1 論文詳解" 背景; "线性注意力状态量化难题" 时间维度), d_k = d_v
+= 128, per-head 4/6/8-bit codes averaging 6 bits plus 32 FP16 pivot heads
+(1.39 %), bf16 q/k/v, synthetic seeded inputs.  One step = one call of
+sq_decode_step over the whole batch (one kernel launch): every tile is read,
+updated, read out, requantized and written back in place.
+
+Prints ONE JSON line: heads*tokens/s, ms per step, algorithmic HBM GB/s, the
+roofline of the step kernel, and the CPU oracle timed on a bounded sample of
+the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized state-update heads·tokens/s + achieved HBM GB/s (70 req × 2304 heads)"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "quantized_recurrent_state_gated_amd", "csrc", "sq_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step128_serving.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes_per_step(w, bits) -> int:
+    """State read + write of every tile, plus per head-token q, k, v (bf16),
+    alpha, beta (fp32) and o (fp32)."""
+    d2 = w.dk * w.dv
+    state = sum(2 * d2 * int(b) // 8 for b in bits) * w.n_req
+    io = w.n_req * w.n_heads * (2 * (2 * w.dk + w.dv) + 8 + 4 * w.dv)
+    return state + io
+
+
+def traffic_from_profile(sha: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this exact kernel
+    source, scaled by the copy-kernel calibration; None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
+    """The oracle, as it stands, on a bounded sample: whole requests (all 2304
+    heads) of the same workload, calibrated to about target_s seconds."""
+    import numpy as np
+    import oracle
+
+    off, slab = oracle.pool_layout(bits, w.dk, w.dv)
+    q = si.q.float().cpu().numpy()
+    k = si.k.float().cpu().numpy()
+    v = si.v.float().cpu().numpy()
+    al = si.alpha.cpu().numpy()
+    be = si.beta.cpu().numpy()
+
+    def run(n):
+        slots = np.arange(n, dtype=np.int32)
+        pool = get_pool(n)
+        t0 = time.perf_counter()
+        oracle.step_pool(pool, bits, w.dk, w.dv, r, c, slots, q[:n], k[:n], v[:n], al[:n], be[:n],
+                         n_threads=n_threads)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = max(1, min(w.n_req, int(target_s / max(t1, 1e-3))))
+    tn = run(n) if n > 1 else t1
+    return {"value": n * w.n_heads / tn, "unit": "heads*tokens/s", "cores": n_threads,
+            "kind": "oracle",
+            "sample": f"{n} of {w.n_req} requests x all {w.n_heads} heads, one decode step "
+                      f"({n * w.n_heads} tiles, {tn:.1f} s wall on {n_threads} threads)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="serving", choices=["serving", "highconc", "layer", "drift"])
+    ap.add_argument("--distinct-inputs", type=int, default=16,
+                    help="distinct pre-generated step inputs, cycled over the timed steps")
+    ap.add_argument("--cpu-threads", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the step shards by request slot or by "
+              "head with no exchange; multi-GPU runs are not part of it)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from quantized_recurrent_state_gated_amd import inputs as I
+    from quantized_recurrent_state_gated_amd import sq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = I.WORKLOADS[args.workload]
+    bits = I.head_bits(w)
+    log(f"[bench] workload {w.name}: {w.n_req} req x {w.n_heads} heads, d={w.dk}, "
+        f"bits { {int(b): int((bits == b).sum()) for b in sorted(set(bits))} }")
+
+    t0 = time.time()
+    r, c = I.scales(w, device=dev)
+    nbytes = sq.sq_pool_bytes(w.n_req, w.n_heads, w.dk, w.dv, bits)
+    state = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pool = sq.sq_pool_alloc(w.n_req, w.n_heads, w.dk, w.dv, bits, r, c, state)
+    slots = torch.arange(w.n_req, dtype=torch.int32, device=dev)
+    for p in range(w.n_req):
+        sq.sq_pool_store(pool, slots[p:p + 1], I.initial_state(w, p, dev))
+    torch.cuda.synchronize()
+    log(f"[bench] pool {nbytes / 1e9:.3f} GB initialised in {time.time() - t0:.1f} s")
+
+    n_in = max(1, min(args.distinct_inputs, args.steps))
+    ins = [I.step_inputs(w, t, dev) for t in range(n_in)]
+    o = torch.empty(w.n_req, w.n_heads, w.dv, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {n_in} distinct step inputs resident in HBM")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    stream = torch.cuda.current_stream()
+
+    def step(t):
+        x = ins[t % n_in]
+        sq.sq_decode_step(pool, slots, x.q, x.k, x.v, x.alpha, x.beta, o, stream)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for t in range(args.steps):
+        step(args.warmup + t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    log(f"[bench] {args.steps} timed steps: {gpu_ms:.3f} ms events, {wall * 1e3:.3f} ms wall")
+
+    head_tokens = w.n_req * w.n_heads
+    value = head_tokens * args.steps / (gpu_ms / 1e3)
+    bpstep = algorithmic_bytes_per_step(w, bits)
+    gbps = bpstep / (ms_per_step / 1e3) / 1e9
+    sha = kernel_source_sha()
+    traffic = traffic_from_profile(sha)
+    stats = I.pool_stats(w)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "heads*tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.n_req} requests x {w.n_heads} heads, d_k=d_v={w.dk}, "
+                        f"4/6/8-bit codes (mean {stats['mean_bits_nonpivot']:.3f}) + FP16 pivots, "
+                        f"{w.qkv_dtype} q/k/v, one fused decode step per launch",
+            "n_req": w.n_req, "n_heads": w.n_heads, "d_k": w.dk, "d_v": w.dv,
+            "head_bits": {str(int(b)): int((bits == b).sum()) for b in sorted(set(bits))},
+            "pool_bytes": stats["pool_bytes"],
+            "state_compression_vs_fp32": stats["fp32_pool_bytes"] / stats["pool_bytes"],
+        },
+        "hbm_gbps": gbps,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": "k_step128 (one launch = one decode step over all tiles)",
+            "algorithmic_bytes_per_launch": bpstep,
+            "avg_launch_ms": ms_per_step,
+            "kernel_source_sha": sha,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        del ins
+        torch.cuda.synchronize()
+        log("[bench] CPU oracle baseline ...")
+        n_cpu = args.cpu_threads or min(len(os.sched_getaffinity(0)), 16)
+        si = I.step_inputs(w, 0, dev)
+        slab = nbytes // w.n_req
+
+        def get_pool(n):
+            return state[: n * slab].cpu().numpy()
+
+        result["cpu_baseline"] = cpu_baseline(w, bits, get_pool, r.cpu().numpy(), c.cpu().numpy(),
+                                              si, n_cpu, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {result['cpu_baseline']['value']:.3e} heads*tokens/s")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,156 @@
+/*
+ * sq.h -- C ABI of libsq: the fused quantized gated delta-rule decode step
+ * over a per-request pool of low-bit recurrent states, for AMD MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [P1] "K1 論文詳解" (k1-news, paper of 2026-10-09), STEPQuant article,
+ *        sections 背景 (background), 方法 (method), 實驗結果 (results).
+ *   [P5] "线性注意力状态量化难题:Qwen状态池70并发就超模型权重" (aitest123),
+ *        sections 直接量化为什么会翻车, 时间维度, 空间维度, 工程落地.
+ *
+ * What one decode step computes, per request n (owning slot p = slot_ids[n])
+ * and head h, on that head's d_k x d_v state S (rows = key dims, columns =
+ * value dims, [P5] 空间维度):
+ *     S^ = decode(tile(p, h))                   stored codes -> real state
+ *     u  = S^T k
+ *     S' = alpha S^ + beta k (v - alpha u)^T    = alpha (I - beta k k^T) S^ + beta k v^T
+ *     o  = S'^T q                                readout, before requantization
+ *     tile(p, h) = encode(S')                    requantize + repack, in place
+ * The update is the gated delta rule ([P5] opening and 时间维度: decay by the
+ * gate, correction along the current key); every step reads, updates,
+ * requantizes and stores the state ([P5] 直接量化为什么会翻车).
+ *
+ * STATE FORMAT (public; the CPU reference implements it independently)
+ *   head_bits[h] selects the storage of head h:
+ *     4, 6, 8  integer codes q in [-Q, Q], Q = 2^(b-1) - 1 ([P5]
+ *              直接量化为什么会翻车: 4/6/8-bit integers), stored as the
+ *              unsigned field q + 2^(b-1);
+ *     16       FP16 "pivot" head, IEEE binary16, unquantized ([P1] 方法;
+ *              [P5] 时间维度: the riskiest heads stay FP16);
+ *     32       FP32 state, unquantized (the full-precision baseline path).
+ *   Dequantization uses a per-key-row factor times a per-value-column factor
+ *   ([P5] 空间维度; [P1] 方法): S^_ij = q_ij * s_ij, s_ij = fl32(r_i * c_j).
+ *   Requantization: q = clamp(rne(S'_ij / s_ij), -Q, Q) (round half to even).
+ *   FP16 pivots round S' to binary16 (half to even).
+ *   Tile layout: element (i, j) is field number
+ *       n = 16 * ((i/4) * (d_v/4) + j/4) + 4 * (j%4) + (i%4)
+ *   (4x4 blocks in block-row order; inside a block the four rows of a column
+ *   are consecutive), and field n occupies bits [n*w, n*w + w) of the tile
+ *   read as a little-endian bit stream, w = head_bits[h].  So 4-bit codes sit
+ *   two per byte and 6-bit codes four per three bytes; a tile is
+ *   d_k*d_v*w/8 bytes.  A slot's slab holds heads 0..H-1 in order, each tile
+ *   starting on a 256-byte boundary; slot p's slab starts at p * slab_bytes.
+ *
+ * CONVENTIONS
+ *   - Every function returns an sq_status (int); nothing throws across the ABI.
+ *   - Host-checkable argument errors are reported before any HIP call is made.
+ *   - Device pointers are borrowed: the caller allocates and frees them (for
+ *     example as torch tensors).  The library owns only the sq_pool object and
+ *     the small device tables it allocates in sq_pool_alloc.
+ *   - All device work is enqueued on the caller's stream (a hipStream_t passed
+ *     as void*, NULL = the null stream); no call synchronizes.  Results are
+ *     visible after the caller synchronizes that stream.  Calls that touch the
+ *     same pool must be ordered on one stream.
+ *   - A slot must not appear twice in one slot_ids batch: two workgroups would
+ *     update the same tile (undefined result).  Slot ids are not checked on
+ *     the device.
+ *   - Non-finite inputs (alpha, beta, q, k, v, scales) are a caller error; the
+ *     resulting codes are unspecified but stay in the code range.
+ *   - d_k and d_v must be multiples of 4 and at most 256; d_k = d_v = 128 takes
+ *     the tuned kernels, other shapes a plain one.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sq_pool sq_pool; /* opaque handle */
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_INVALID = -1,     /* null pointer, bad size, misaligned pointer, buffer too small */
+    SQ_ERR_UNSUPPORTED = -2, /* bit width not in {4,6,8,16,32}, or d_k/d_v not supported */
+    SQ_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+    SQ_ERR_NOMEM = -4        /* host or device allocation of the pool's tables failed */
+} sq_status;
+
+typedef enum {
+    SQ_F32 = 0, /* IEEE binary32 */
+    SQ_BF16 = 1 /* bfloat16, upcast exactly to fp32 on load */
+} sq_dtype;
+
+typedef struct {
+    int32_t n_slots;          /* number of resident request states (slots), >= 1 */
+    int32_t n_heads;          /* recurrent heads per request, >= 1 */
+    int32_t d_k, d_v;         /* state rows (key dims) and columns (value dims) */
+    const uint8_t *head_bits; /* HOST [n_heads], each in {4, 6, 8, 16, 32}; copied */
+    const float *row_scale;   /* DEVICE [n_heads][d_k] fp32, r_i > 0; borrowed, read by
+                                 every call; entries of 16/32-bit heads are ignored */
+    const float *col_scale;   /* DEVICE [n_heads][d_v] fp32, c_j > 0; as row_scale */
+    void *state;              /* DEVICE, 256-byte aligned, >= sq_pool_bytes(...) bytes,
+                                 laid out as described above; borrowed */
+    uint64_t state_bytes;     /* size of the state buffer in bytes */
+} sq_pool_desc;
+
+/* Bytes the state buffer needs for this shape: n_slots * slab_bytes.
+ * Returns 0 if any argument is invalid or unsupported.  Host only. */
+uint64_t sq_pool_bytes(int32_t n_slots, int32_t n_heads, int32_t d_k, int32_t d_v,
+                       const uint8_t *head_bits);
+
+/* Validate desc, compute the tile offsets and upload them (and the per-width
+ * head lists) to a small device table.  On success *out receives a handle to
+ * release with sq_pool_free.  Errors: SQ_ERR_INVALID (null desc/out/pointers,
+ * n_slots or n_heads < 1, state not 256-byte aligned, scales not 16-byte
+ * aligned, state_bytes too small), SQ_ERR_UNSUPPORTED (bits, d_k, d_v),
+ * SQ_ERR_NOMEM, SQ_ERR_HIP.  Synchronous (uploads with a blocking copy). */
+int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out);
+
+/* Release the handle and its device table (not the borrowed buffers).
+ * NULL is a no-op.  The caller must ensure no enqueued work still uses it. */
+void sq_pool_free(sq_pool *pool);
+
+/* Byte offset and size of tile (slot, head) inside the state buffer.
+ * Host only; SQ_ERR_INVALID for a null pool/out pointer or out-of-range ids. */
+int sq_pool_tile_offset(const sq_pool *pool, int32_t slot, int32_t head, uint64_t *offset,
+                        uint64_t *bytes);
+
+/* Quantize-and-store: encode fp32 states S (DEVICE, [n_req][n_heads][d_k][d_v],
+ * row-major) into the tiles of slots slot_ids[0..n_req) (DEVICE int32), with
+ * the quantizer and layout above (the hand-off of a state computed elsewhere,
+ * e.g. at prefill).  n_req == 0 is a no-op.  Asynchronous on `stream`. */
+int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const float *S,
+                  void *stream);
+
+/* One fused decode step for a batch of n_req requests (see the top of this
+ * file).  All pointers DEVICE, row-major:
+ *   slot_ids int32 [n_req], each in [0, n_slots), no duplicates;
+ *   q, k     [n_req][n_heads][d_k] of qkv_dtype (sq_dtype);
+ *   v        [n_req][n_heads][d_v] of qkv_dtype;
+ *   alpha, beta fp32 [n_req][n_heads] (gate in (0, 1], write strength in [0, 1]);
+ *   o        fp32 [n_req][n_heads][d_v], written with S'^T q; may be NULL.
+ * q/k/v/o must be 16-byte aligned.  The pool's tiles are updated in place.
+ * n_req == 0 is a no-op.  Asynchronous on `stream`. */
+int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
+                   const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
+                   const float *beta, float *o, void *stream);
+
+/* Readout without update: o = S^T q from the stored state (dequantized), for
+ * slots slot_ids[0..n_req).  q: DEVICE [n_req][n_heads][d_k] of q_dtype;
+ * o: DEVICE fp32 [n_req][n_heads][d_v].  Does not modify the pool.  n_req == 0
+ * is a no-op.  Asynchronous on `stream`. */
+int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
+               int32_t q_dtype, float *o, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *sq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

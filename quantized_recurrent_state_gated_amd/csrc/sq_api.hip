@@ -1,0 +1,282 @@
+// sq_api.hip -- host side of libsq: argument validation, pool layout, the
+// small device table, and kernel dispatch per width class.  See include/sq.h
+// for the contract of every entry point.
+//
+// Sources: [P1] "K1 論文詳解" (k1-news, 2026-10-09), 背景 / 方法;
+//          [P5] "线性注意力状态量化难题:Qwen状态池70并发就超模型权重" (aitest123),
+//          opening (one resident state per concurrent request), 时间维度
+//          (per-head bit widths, FP16 pivots), 空间维度 (row x column factors).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/sq.h"
+#include "sq_launch.h"
+
+namespace {
+
+constexpr int kClasses[5] = {4, 6, 8, 16, 32};
+
+int class_index(int bits)
+{
+    for (int c = 0; c < 5; c++)
+        if (kClasses[c] == bits) return c;
+    return -1;
+}
+
+bool shape_ok(int32_t dk, int32_t dv)
+{
+    return dk >= 4 && dv >= 4 && dk <= 256 && dv <= 256 && dk % 4 == 0 && dv % 4 == 0;
+}
+
+uint64_t tile_bytes(int bits, int32_t dk, int32_t dv)
+{
+    return (uint64_t)dk * (uint64_t)dv * (uint64_t)bits / 8;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validate the per-pool shape; fills offsets and the slab size on success.
+int layout(int32_t n_heads, int32_t dk, int32_t dv, const uint8_t *head_bits,
+           std::vector<int64_t> *off, uint64_t *slab)
+{
+    if (n_heads < 1 || !head_bits) return SQ_ERR_INVALID;
+    if (!shape_ok(dk, dv)) return SQ_ERR_UNSUPPORTED;
+    uint64_t o = 0;
+    for (int32_t h = 0; h < n_heads; h++) {
+        if (class_index(head_bits[h]) < 0) return SQ_ERR_UNSUPPORTED;
+        if (off) off->push_back((int64_t)o);
+        o += align256(tile_bytes(head_bits[h], dk, dv));
+    }
+    *slab = o;
+    return SQ_OK;
+}
+
+}  // namespace
+
+struct sq_pool {
+    int32_t n_slots, n_heads, dk, dv;
+    std::vector<uint8_t> bits;
+    std::vector<int64_t> off;
+    uint64_t slab;
+    const float *rsc, *csc;
+    uint8_t *state;
+    uint64_t state_bytes;
+    int device;
+    void *dtab;               // device: int64 head_off[H] | int32 heads grouped by class
+    int64_t *d_off;
+    int32_t *d_heads[5];
+    int32_t n_class[5];
+};
+
+extern "C" {
+
+uint64_t sq_pool_bytes(int32_t n_slots, int32_t n_heads, int32_t d_k, int32_t d_v,
+                       const uint8_t *head_bits)
+{
+    uint64_t slab = 0;
+    if (n_slots < 1) return 0;
+    if (layout(n_heads, d_k, d_v, head_bits, nullptr, &slab) != SQ_OK) return 0;
+    return slab * (uint64_t)n_slots;
+}
+
+int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
+{
+    if (!desc || !out) return SQ_ERR_INVALID;
+    *out = nullptr;
+    const sq_pool_desc &d = *desc;
+    if (d.n_slots < 1 || d.n_heads < 1 || !d.head_bits || !d.state) return SQ_ERR_INVALID;
+    if (!d.row_scale || !d.col_scale) return SQ_ERR_INVALID;
+    if (!aligned(d.state, 256) || !aligned(d.row_scale, 16) || !aligned(d.col_scale, 16))
+        return SQ_ERR_INVALID;
+    std::vector<int64_t> off;
+    uint64_t slab = 0;
+    int st = layout(d.n_heads, d.d_k, d.d_v, d.head_bits, &off, &slab);
+    if (st != SQ_OK) return st;
+    if (d.state_bytes < slab * (uint64_t)d.n_slots) return SQ_ERR_INVALID;
+
+    sq_pool *p = new (std::nothrow) sq_pool();
+    if (!p) return SQ_ERR_NOMEM;
+    p->n_slots = d.n_slots;
+    p->n_heads = d.n_heads;
+    p->dk = d.d_k;
+    p->dv = d.d_v;
+    p->bits.assign(d.head_bits, d.head_bits + d.n_heads);
+    p->off = off;
+    p->slab = slab;
+    p->rsc = d.row_scale;
+    p->csc = d.col_scale;
+    p->state = static_cast<uint8_t *>(d.state);
+    p->state_bytes = d.state_bytes;
+
+    // host image of the device table: offsets, then head ids grouped by width
+    const size_t H = (size_t)d.n_heads;
+    std::vector<unsigned char> img(H * 8 + H * 4);
+    memcpy(img.data(), off.data(), H * 8);
+    int32_t *heads = reinterpret_cast<int32_t *>(img.data() + H * 8);
+    size_t pos = 0;
+    size_t start[5];
+    for (int c = 0; c < 5; c++) {
+        start[c] = pos;
+        p->n_class[c] = 0;
+        for (int32_t h = 0; h < d.n_heads; h++)
+            if (d.head_bits[h] == kClasses[c]) {
+                heads[pos++] = h;
+                p->n_class[c]++;
+            }
+    }
+    if (hipGetDevice(&p->device) != hipSuccess) {
+        delete p;
+        return SQ_ERR_HIP;
+    }
+    if (hipMalloc(&p->dtab, img.size()) != hipSuccess) {
+        delete p;
+        return SQ_ERR_NOMEM;
+    }
+    if (hipMemcpy(p->dtab, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(p->dtab);
+        delete p;
+        return SQ_ERR_HIP;
+    }
+    p->d_off = static_cast<int64_t *>(p->dtab);
+    int32_t *dheads = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(p->dtab) + H * 8);
+    for (int c = 0; c < 5; c++) p->d_heads[c] = dheads + start[c];
+    *out = p;
+    return SQ_OK;
+}
+
+void sq_pool_free(sq_pool *pool)
+{
+    if (!pool) return;
+    if (pool->dtab) (void)hipFree(pool->dtab);
+    delete pool;
+}
+
+int sq_pool_tile_offset(const sq_pool *pool, int32_t slot, int32_t head, uint64_t *offset,
+                        uint64_t *bytes)
+{
+    if (!pool || !offset || !bytes) return SQ_ERR_INVALID;
+    if (slot < 0 || slot >= pool->n_slots || head < 0 || head >= pool->n_heads)
+        return SQ_ERR_INVALID;
+    *offset = (uint64_t)slot * pool->slab + (uint64_t)pool->off[head];
+    *bytes = tile_bytes(pool->bits[head], pool->dk, pool->dv);
+    return SQ_OK;
+}
+
+static sqk::StepArgs base_args(const sq_pool *p, const int32_t *slot_ids)
+{
+    sqk::StepArgs a;
+    memset(&a, 0, sizeof(a));
+    a.pool = p->state;
+    a.slab = p->slab;
+    a.head_off = p->d_off;
+    a.H = p->n_heads;
+    a.dk = p->dk;
+    a.dv = p->dv;
+    a.slot_ids = slot_ids;
+    a.rsc = p->rsc;
+    a.csc = p->csc;
+    return a;
+}
+
+static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16, int32_t n_req,
+                       void *stream)
+{
+    // heaviest tiles first: FP32, FP16 pivots, then 8-, 6- and 4-bit heads
+    static const int order[5] = {4, 3, 2, 1, 0};
+    if (op != sqk::OP_STORE && p->dk == 128 && p->dv == 128) {
+        sqk::FusedArgs f;
+        memset(&f, 0, sizeof(f));
+        f.a = a;
+        uint64_t total = 0;
+        for (int oc = 0; oc < 5; oc++) {
+            const int c = order[oc];
+            if (p->n_class[c] == 0) continue;
+            const int i = f.n_classes++;
+            f.heads[i] = p->d_heads[c];
+            f.Hc[i] = p->n_class[c];
+            f.bits[i] = kClasses[c];
+            f.start[i] = (uint32_t)total;
+            total += (uint64_t)n_req * (uint64_t)p->n_class[c];
+        }
+        if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
+        if (sqk::launch_fused128(op, bf16, f, (uint32_t)total, (hipStream_t)stream) != hipSuccess)
+            return SQ_ERR_HIP;
+        return SQ_OK;
+    }
+    for (int oc = 0; oc < 5; oc++) {
+        const int c = order[oc];
+        if (p->n_class[c] == 0) continue;
+        a.heads = p->d_heads[c];
+        a.Hc = p->n_class[c];
+        if (sqk::launch(op, kClasses[c], bf16, a, n_req, (hipStream_t)stream) != hipSuccess)
+            return SQ_ERR_HIP;
+    }
+    return SQ_OK;
+}
+
+int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const float *S,
+                  void *stream)
+{
+    if (!pool || n_req < 0) return SQ_ERR_INVALID;
+    if (n_req == 0) return SQ_OK;
+    if (n_req > pool->n_slots || !slot_ids || !S || !aligned(S, 16)) return SQ_ERR_INVALID;
+    sqk::StepArgs a = base_args(pool, slot_ids);
+    a.S = S;
+    return run_classes(pool, sqk::OP_STORE, a, false, n_req, stream);
+}
+
+int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
+                   const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
+                   const float *beta, float *o, void *stream)
+{
+    if (!pool || n_req < 0) return SQ_ERR_INVALID;
+    if (qkv_dtype != SQ_F32 && qkv_dtype != SQ_BF16) return SQ_ERR_INVALID;
+    if (n_req == 0) return SQ_OK;
+    if (n_req > pool->n_slots || !slot_ids || !q || !k || !v || !alpha || !beta)
+        return SQ_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (o && !aligned(o, 16)))
+        return SQ_ERR_INVALID;
+    sqk::StepArgs a = base_args(pool, slot_ids);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.o = o;
+    return run_classes(pool, sqk::OP_STEP, a, qkv_dtype == SQ_BF16, n_req, stream);
+}
+
+int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
+               int32_t q_dtype, float *o, void *stream)
+{
+    if (!pool || n_req < 0) return SQ_ERR_INVALID;
+    if (q_dtype != SQ_F32 && q_dtype != SQ_BF16) return SQ_ERR_INVALID;
+    if (n_req == 0) return SQ_OK;
+    if (n_req > pool->n_slots || !slot_ids || !q || !o || !aligned(q, 16) || !aligned(o, 16))
+        return SQ_ERR_INVALID;
+    sqk::StepArgs a = base_args(pool, slot_ids);
+    a.q = q;
+    a.o = o;
+    return run_classes(pool, sqk::OP_READOUT, a, q_dtype == SQ_BF16, n_req, stream);
+}
+
+const char *sq_status_string(int status)
+{
+    switch (status) {
+    case SQ_OK: return "ok";
+    case SQ_ERR_INVALID: return "invalid argument";
+    case SQ_ERR_UNSUPPORTED: return "unsupported bit width or shape";
+    case SQ_ERR_HIP: return "HIP runtime error";
+    case SQ_ERR_NOMEM: return "out of memory";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

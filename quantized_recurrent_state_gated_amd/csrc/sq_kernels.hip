@@ -1,0 +1,595 @@
+// sq_kernels.hip -- gfx950 kernels of the fused quantized gated delta-rule
+// decode step.
+//
+// Sources (cited by title and section):
+//   [P1] "K1 論文詳解" (k1-news, 2026-10-09), STEPQuant article, 方法.
+//   [P5] "线性注意力状态量化难题:Qwen状态池70并发就超模型权重" (aitest123),
+//        直接量化为什么会翻车, 时间维度, 空间维度, 工程落地.
+//
+// The step is one rank-1 update per (request, head) tile, so it is bound by
+// HBM bandwidth, not by arithmetic: the pages fuse quantization with the state
+// update precisely to cut memory traffic ([P1] 方法, last paragraph; [P5]
+// 工程落地).  Here every tile is streamed from HBM once and written back once;
+// there is no MFMA (nothing here is a dense contraction).
+//
+// Arithmetic is done in the code domain.  With Shat_ij = q_ij r_i c_j and the
+// update S' = alpha Shat + beta k (v - alpha u)^T, u = Shat^T k:
+//     u_j  = c_j * sum_i (k_i r_i) q_ij                 (column reduction)
+//     y_j  = c_j * sum_i (q_i r_i) q_ij                 (readout of Shat)
+//     S'_ij / (r_i c_j) = alpha q_ij + a_i b_j,  a_i = beta k_i / r_i,
+//                                                 b_j = (v_j - alpha u_j) / c_j
+//     o_j  = alpha y_j + beta (q.k) (v_j - alpha u_j)   ( = sum_i q_i S'_ij )
+// so the tile is touched by two fused multiply-adds per element per pass and
+// o needs no second reduction.  Codes are carried in their stored excess form
+// n = q + 2^(b-1); the bias is folded into per-tile constants.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sq_launch.h"
+
+namespace sqk {
+
+// ---------------------------------------------------------------- loads
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T *p, long i);
+template <>
+__device__ __forceinline__ float ld1<float>(const float *p, long i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld1<uint16_t>(const uint16_t *p, long i)
+{
+    return __uint_as_float((uint32_t)p[i] << 16);  // bf16 -> fp32 is exact
+}
+
+template <typename T>
+__device__ __forceinline__ void ld4(const T *p, long i, float (&x)[4]);
+template <>
+__device__ __forceinline__ void ld4<float>(const float *p, long i, float (&x)[4])
+{
+    float4 f = *reinterpret_cast<const float4 *>(p + i);
+    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+}
+template <>
+__device__ __forceinline__ void ld4<uint16_t>(const uint16_t *p, long i, float (&x)[4])
+{
+    uint2 u = *reinterpret_cast<const uint2 *>(p + i);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------- block codec
+//
+// A 4x4 block is 16 consecutive fields, field e = 4*col + row, packed LSB
+// first; it is BITS/2 dwords long.  decode() yields each field as a float:
+// the excess-form code n for 4/6/8 bits, the value itself for 16/32 bits.
+// encode() takes the updated value in the same form; codes are clamped to
+// [1, 2^b - 1] (the symmetric range) and rounded half to even.
+
+template <int BITS>
+struct Codec {
+    static constexpr int W = BITS / 2;
+};
+
+template <int BITS>
+__device__ __forceinline__ void decode(const uint32_t (&d)[BITS / 2], float (&f)[16])
+{
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) f[e] = (float)((d[e >> 2] >> (8 * (e & 3))) & 0xffu);
+    } else if constexpr (BITS == 4) {
+        // split each dword's nibbles into two dwords of bytes, then convert
+        // bytes directly (v_cvt_f32_ubyte0..3)
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            const uint32_t lo = d[w] & 0x0f0f0f0fu, hi = (d[w] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                f[8 * w + 2 * p] = (float)((lo >> (8 * p)) & 0xffu);
+                f[8 * w + 2 * p + 1] = (float)((hi >> (8 * p)) & 0xffu);
+            }
+        }
+    } else if constexpr (BITS == 6) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const int bit = 6 * e, w = bit >> 5, s = bit & 31;
+            uint32_t x;
+            if (s + 6 <= 32)
+                x = d[w] >> s;
+            else
+                x = (d[w] >> s) | (d[w + 1] << (32 - s));
+            f[e] = (float)(x & 0x3fu);
+        }
+    } else if constexpr (BITS == 16) {
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+            f[e] = __half2float(__ushort_as_half((unsigned short)(d[e >> 1] >> (16 * (e & 1)))));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; e++) f[e] = __uint_as_float(d[e]);
+    }
+}
+
+// v_cvt_pk_u8_f32: convert x to an unsigned byte (round half to even,
+// saturating to [0, 255]) and insert it as byte `sel` of `acc`.
+__device__ __forceinline__ uint32_t pk_u8(float x, uint32_t sel, uint32_t acc)
+{
+    return __builtin_amdgcn_cvt_pk_u8_f32(x, sel, acc);
+}
+
+template <int BITS>
+__device__ __forceinline__ float clamp_code(float z)
+{
+    // symmetric range [1, 2^b - 1] in excess form; the upper bound of the
+    // 8-bit range is the conversion's own saturation.  NaN -> 1 (in range).
+    if constexpr (BITS == 8) return fmaxf(z, 1.0f);
+    else return __builtin_amdgcn_fmed3f(z, 1.0f, (float)((1 << BITS) - 1));
+}
+
+template <int BITS>
+__device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[BITS / 2])
+{
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            uint32_t x = pk_u8(clamp_code<8>(z[4 * w]), 0, 0u);
+            x = pk_u8(clamp_code<8>(z[4 * w + 1]), 1, x);
+            x = pk_u8(clamp_code<8>(z[4 * w + 2]), 2, x);
+            d[w] = pk_u8(clamp_code<8>(z[4 * w + 3]), 3, x);
+        }
+    } else if constexpr (BITS == 4) {
+        // even fields into one dword of bytes, odd fields into another, then
+        // interleave the nibbles with one shift-or
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            uint32_t ev = 0u, od = 0u;
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                ev = pk_u8(clamp_code<4>(z[8 * w + 2 * p]), p, ev);
+                od = pk_u8(clamp_code<4>(z[8 * w + 2 * p + 1]), p, od);
+            }
+            d[w] = ev | (od << 4);
+        }
+    } else if constexpr (BITS == 6) {
+        // four codes of a column -> four bytes -> one 24-bit group, then the
+        // four groups are spliced into three dwords
+        uint32_t g[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            uint32_t x = pk_u8(clamp_code<6>(z[4 * c]), 0, 0u);
+            x = pk_u8(clamp_code<6>(z[4 * c + 1]), 1, x);
+            x = pk_u8(clamp_code<6>(z[4 * c + 2]), 2, x);
+            x = pk_u8(clamp_code<6>(z[4 * c + 3]), 3, x);
+            // bytes are < 64: pair them into 12-bit halves, then join the halves
+            const uint32_t a = (x & 0x003f003fu) | ((x >> 2) & 0x0fc00fc0u);
+            g[c] = __builtin_amdgcn_ubfe(a, 0, 12) | ((a >> 4) & 0x00fff000u);
+        }
+        d[0] = g[0] | (g[1] << 24);
+        d[1] = (g[1] >> 8) | (g[2] << 16);
+        d[2] = (g[2] >> 16) | (g[3] << 8);
+    } else if constexpr (BITS == 16) {
+#pragma unroll
+        for (int w = 0; w < 8; w++) {
+            const uint32_t lo = __half_as_ushort(__float2half_rn(z[2 * w]));
+            const uint32_t hi = __half_as_ushort(__float2half_rn(z[2 * w + 1]));
+            d[w] = lo | (hi << 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; e++) d[e] = __float_as_uint(z[e]);
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[BITS / 2])
+{
+    if constexpr (BITS == 4) {
+        uint2 x = *reinterpret_cast<const uint2 *>(p);
+        d[0] = x.x; d[1] = x.y;
+    } else if constexpr (BITS == 6) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+        d[0] = q[0]; d[1] = q[1]; d[2] = q[2];
+    } else {
+#pragma unroll
+        for (int w = 0; w < BITS / 2; w += 4) {
+            uint4 x = *reinterpret_cast<const uint4 *>(p + 4 * w);
+            d[w] = x.x; d[w + 1] = x.y; d[w + 2] = x.z; d[w + 3] = x.w;
+        }
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[BITS / 2])
+{
+    if constexpr (BITS == 4) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(d[0], d[1]);
+    } else if constexpr (BITS == 6) {
+        uint32_t *q = reinterpret_cast<uint32_t *>(p);
+        q[0] = d[0]; q[1] = d[1]; q[2] = d[2];
+    } else {
+#pragma unroll
+        for (int w = 0; w < BITS / 2; w += 4)
+            *reinterpret_cast<uint4 *>(p + 4 * w) = make_uint4(d[w], d[w + 1], d[w + 2], d[w + 3]);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s, 64);
+    return x;
+}
+
+// ---------------------------------------------------------------- d = 128 step
+//
+// One 256-thread workgroup per (request, head) tile.  Thread t owns column
+// block cb = t % 32 (columns 4cb..4cb+3) and row group rg = t / 32, i.e. the
+// four 4x4 blocks in block rows rg, rg+8, rg+16, rg+24 (16 rows).  For a
+// fixed m the 64 lanes of a wave read 64 consecutive blocks, so every load
+// and store instruction of a wave covers one contiguous 512 B .. 4 KB span.
+// Partial column sums over a thread's 16 rows are combined across the 8 row
+// groups through LDS.  All width classes run in one launch: the grid is the
+// concatenation of the classes' tiles, heaviest tiles first.
+
+struct Smem128 {
+    float w[128], g[128], a[128];  // per-row factors k_i r_i, q_i r_i, beta k_i / r_i
+    float red[8][8][32];           // [row group][u0..u3, y0..y3][column block]
+    float tot[8][32];
+    float sum[2][3];               // per-wave partials of q.k, sum w, sum g
+};
+
+template <int BITS, typename T, bool UPDATE>
+__device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128 &sm)
+{
+    constexpr int W = BITS / 2;
+    constexpr bool QUANT = BITS <= 8;
+    constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
+    constexpr int BLK_BYTES = 2 * BITS;
+
+    const int t = threadIdx.x;
+    const int cb = t & 31, rg = t >> 5;
+    const long nh = (long)n * a.H + h;
+    const int slot = a.slot_ids[n];
+    uint8_t *tile = a.pool + (uint64_t)slot * a.slab + (uint64_t)a.head_off[h];
+    const T *q = reinterpret_cast<const T *>(a.q);
+    const T *k = reinterpret_cast<const T *>(a.k);
+    const T *v = reinterpret_cast<const T *>(a.v);
+
+    // the tile: 4 blocks per thread, issued first
+    uint32_t d[4][W];
+#pragma unroll
+    for (int m = 0; m < 4; m++) load_block<BITS>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
+
+    const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
+    const float beta = UPDATE ? a.beta[nh] : 0.0f;
+
+    // per-row factors (threads 0..127, one row each) and the three tile sums
+    if (t < 128) {
+        const float qi = ld1(q, nh * 128 + t);
+        const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
+        const float ri = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
+        const float wi = ki * ri, gi = qi * ri;
+        sm.w[t] = wi;
+        sm.g[t] = gi;
+        if (UPDATE) sm.a[t] = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
+        if ((t & 63) == 0) {
+            sm.sum[t >> 6][0] = s0;
+            sm.sum[t >> 6][1] = s1;
+            sm.sum[t >> 6][2] = s2;
+        }
+    }
+    float cc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (QUANT) ld4<float>(a.csc, (long)h * 128 + 4 * cb, cc);
+    float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (UPDATE) ld4<T>(v, nh * 128 + 4 * cb, vv);
+    __syncthreads();
+
+    // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
+    float f[4][16];
+#pragma unroll
+    for (int m = 0; m < 4; m++) decode<BITS>(d[m], f[m]);
+    float pu[4] = {0, 0, 0, 0}, py[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const int i0 = 4 * (rg + 8 * m);
+#pragma unroll
+        for (int ri = 0; ri < 4; ri++) {
+            const float w = sm.w[i0 + ri], g = sm.g[i0 + ri];
+#pragma unroll
+            for (int cj = 0; cj < 4; cj++) {
+                if (UPDATE) pu[cj] = fmaf(w, f[m][4 * cj + ri], pu[cj]);
+                py[cj] = fmaf(g, f[m][4 * cj + ri], py[cj]);
+            }
+        }
+    }
+#pragma unroll
+    for (int cj = 0; cj < 4; cj++) {
+        sm.red[rg][cj][cb] = pu[cj];
+        sm.red[rg][4 + cj][cb] = py[cj];
+    }
+    __syncthreads();
+    {
+        const int e = t >> 5, c2 = t & 31;
+        float s = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; r++) s += sm.red[r][e][c2];
+        sm.tot[e][c2] = s;
+    }
+    __syncthreads();
+
+    const float qk = sm.sum[0][0] + sm.sum[1][0];
+    const float Wsum = sm.sum[0][1] + sm.sum[1][1];
+    const float Gsum = sm.sum[0][2] + sm.sum[1][2];
+    float u[4], y[4];
+#pragma unroll
+    for (int cj = 0; cj < 4; cj++) {
+        u[cj] = cc[cj] * (sm.tot[cj][cb] - OFF * Wsum);
+        y[cj] = cc[cj] * (sm.tot[4 + cj][cb] - OFF * Gsum);
+    }
+    float *o = a.o ? a.o + nh * 128 + 4 * cb : nullptr;
+    if (!UPDATE) {
+        if (rg == 0) *reinterpret_cast<float4 *>(o) = make_float4(y[0], y[1], y[2], y[3]);
+        return;
+    }
+    float b[4], ov[4];
+#pragma unroll
+    for (int cj = 0; cj < 4; cj++) {
+        const float e = vv[cj] - alpha * u[cj];
+        ov[cj] = fmaf(alpha, y[cj], beta * qk * e);
+        b[cj] = QUANT ? e * __builtin_amdgcn_rcpf(cc[cj]) : e;
+    }
+    if (o && rg == 0) *reinterpret_cast<float4 *>(o) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+
+    // pass 2: z = alpha n + a_i b_j + OFF (1 - alpha), requantize, repack, store
+    const float C = OFF * (1.0f - alpha);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const int i0 = 4 * (rg + 8 * m);
+        float z[16];
+#pragma unroll
+        for (int ri = 0; ri < 4; ri++) {
+            const float ai = sm.a[i0 + ri];
+#pragma unroll
+            for (int cj = 0; cj < 4; cj++)
+                z[4 * cj + ri] = fmaf(alpha, f[m][4 * cj + ri], fmaf(ai, b[cj], C));
+        }
+        uint32_t dn[W];
+        encode<BITS>(z, dn);
+        store_block<BITS>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, dn);
+    }
+}
+
+template <typename T, bool UPDATE>
+__global__ __launch_bounds__(256) void k_step128(FusedArgs f)
+{
+    __shared__ Smem128 sm;
+    const uint32_t b = blockIdx.x;
+    int c = 0;
+#pragma unroll
+    for (int i = 1; i < 5; i++)
+        if (i < f.n_classes && b >= f.start[i]) c = i;
+    const uint32_t local = b - f.start[c];
+    const int n = (int)(local / (uint32_t)f.Hc[c]);
+    const int h = f.heads[c][local - (uint32_t)n * (uint32_t)f.Hc[c]];
+    switch (f.bits[c]) {
+    case 32: tile128<32, T, UPDATE>(f.a, n, h, sm); break;
+    case 16: tile128<16, T, UPDATE>(f.a, n, h, sm); break;
+    case 8: tile128<8, T, UPDATE>(f.a, n, h, sm); break;
+    case 6: tile128<6, T, UPDATE>(f.a, n, h, sm); break;
+    default: tile128<4, T, UPDATE>(f.a, n, h, sm); break;
+    }
+}
+
+// ---------------------------------------------------------------- any shape
+//
+// d_k, d_v multiples of 4 and <= 256.  Plain and unhurried: one workgroup per
+// tile, thread j owns column j for the reductions (reading fields one by
+// one), then threads rewrite whole blocks.
+
+__device__ __forceinline__ uint32_t field_get(const uint8_t *tile, int w, long nidx)
+{
+    const long bit = nidx * w;
+    const long byte = bit >> 3;
+    const int sh = (int)(bit & 7);
+    const int nb = (sh + w + 7) >> 3;
+    uint64_t x = 0;
+    for (int b = 0; b < nb; b++) x |= (uint64_t)tile[byte + b] << (8 * b);
+    x >>= sh;
+    return w == 32 ? (uint32_t)x : (uint32_t)(x & ((1ull << w) - 1));
+}
+
+template <int BITS>
+__device__ __forceinline__ float field_value(uint32_t f)
+{
+    // centred value: code q for 4/6/8 bits, the value for 16/32 bits
+    if constexpr (BITS <= 8) return (float)((int)f - (1 << (BITS - 1)));
+    else if constexpr (BITS == 16) return __half2float(__ushort_as_half((unsigned short)f));
+    else return __uint_as_float(f);
+}
+
+template <int BITS, typename T, bool UPDATE>
+__global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
+{
+    constexpr int W = BITS / 2;
+    constexpr bool QUANT = BITS <= 8;
+    constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
+    __shared__ float sW[256], sG[256], sA[256], sB[256];
+    __shared__ float sQK;
+
+    const int t = threadIdx.x;
+    const int dk = a.dk, dv = a.dv;
+    const int n = blockIdx.x / a.Hc;
+    const int hc = blockIdx.x - n * a.Hc;
+    const int h = a.heads[hc];
+    const long nh = (long)n * a.H + h;
+    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const T *q = reinterpret_cast<const T *>(a.q);
+    const T *k = reinterpret_cast<const T *>(a.k);
+    const T *v = reinterpret_cast<const T *>(a.v);
+    const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
+    const float beta = UPDATE ? a.beta[nh] : 0.0f;
+
+    for (int i = t; i < dk; i += 256) {
+        const float ri = QUANT ? a.rsc[(long)h * dk + i] : 1.0f;
+        const float ki = UPDATE ? ld1(k, nh * dk + i) : 0.0f;
+        sW[i] = ki * ri;
+        sG[i] = ld1(q, nh * dk + i) * ri;
+        sA[i] = QUANT ? beta * ki / ri : beta * ki;
+    }
+    if (t == 0) {
+        float s = 0.0f;
+        for (int i = 0; i < dk; i++) s += ld1(q, nh * dk + i) * (UPDATE ? ld1(k, nh * dk + i) : 0.0f);
+        sQK = s;
+    }
+    __syncthreads();
+    for (int j = t; j < dv; j += 256) {
+        float U = 0.0f, Y = 0.0f;
+        for (int i = 0; i < dk; i++) {
+            const long nidx = 16L * ((i >> 2) * (dv >> 2) + (j >> 2)) + 4 * (j & 3) + (i & 3);
+            const float x = field_value<BITS>(field_get(tile, BITS, nidx));
+            U = fmaf(sW[i], x, U);
+            Y = fmaf(sG[i], x, Y);
+        }
+        const float cj = QUANT ? a.csc[(long)h * dv + j] : 1.0f;
+        const float uj = cj * U, yj = cj * Y;
+        if (!UPDATE) {
+            a.o[nh * dv + j] = yj;
+            continue;
+        }
+        const float e = ld1(v, nh * dv + j) - alpha * uj;
+        if (a.o) a.o[nh * dv + j] = fmaf(alpha, yj, beta * sQK * e);
+        sB[j] = QUANT ? e / cj : e;
+    }
+    if (!UPDATE) return;
+    __syncthreads();
+    const float C = OFF * (1.0f - alpha);
+    const int nblk = (dk >> 2) * (dv >> 2);
+    for (int B = t; B < nblk; B += 256) {
+        const int i0 = 4 * (B / (dv >> 2)), j0 = 4 * (B % (dv >> 2));
+        uint32_t dd[W];
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + (long)B * 2 * BITS);
+#pragma unroll
+        for (int w = 0; w < W; w++) dd[w] = src[w];
+        float f[16], z[16];
+        decode<BITS>(dd, f);
+#pragma unroll
+        for (int cj = 0; cj < 4; cj++)
+#pragma unroll
+            for (int ri = 0; ri < 4; ri++)
+                z[4 * cj + ri] = fmaf(alpha, f[4 * cj + ri], fmaf(sA[i0 + ri], sB[j0 + cj], C));
+        encode<BITS>(z, dd);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(tile + (long)B * 2 * BITS);
+#pragma unroll
+        for (int w = 0; w < W; w++) dst[w] = dd[w];
+    }
+}
+
+// ---------------------------------------------------------------- store
+//
+// Quantize fp32 states into tiles: one thread per 4x4 block.  The code is
+// clamp(rne(x / s), -Q, Q) with s = fl32(r_i c_j) and a correctly rounded
+// fp32 division.
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_store(StepArgs a, long total_blocks)
+{
+    constexpr int W = BITS / 2;
+    constexpr bool QUANT = BITS <= 8;
+    constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= total_blocks) return;
+    const int dk = a.dk, dv = a.dv;
+    const long nblk = (long)(dk >> 2) * (dv >> 2);
+    const long tix = gid / nblk;
+    const long B = gid - tix * nblk;
+    const int n = (int)(tix / a.Hc);
+    const int h = a.heads[tix - (long)n * a.Hc];
+    const long nh = (long)n * a.H + h;
+    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const int i0 = 4 * (int)(B / (dv >> 2)), j0 = 4 * (int)(B % (dv >> 2));
+    const float *S = a.S + nh * (long)dk * dv;
+    float z[16];
+#pragma unroll
+    for (int cj = 0; cj < 4; cj++)
+#pragma unroll
+        for (int ri = 0; ri < 4; ri++) {
+            const float x = S[(long)(i0 + ri) * dv + j0 + cj];
+            if constexpr (QUANT) {
+                const float s = a.rsc[(long)h * dk + i0 + ri] * a.csc[(long)h * dv + j0 + cj];
+                // decision on fl32(x / s), ties to even, then the symmetric clamp
+                const float qf = fminf(fmaxf(__builtin_rintf(x / s), 1.0f - OFF), OFF - 1.0f);
+                z[4 * cj + ri] = qf + OFF;  // integer-valued, exact
+            } else {
+                z[4 * cj + ri] = x;
+            }
+        }
+    uint32_t dd[W];
+    encode<BITS>(z, dd);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(tile + B * 2 * BITS);
+#pragma unroll
+    for (int w = 0; w < W; w++) dst[w] = dd[w];
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <int BITS, typename T>
+static hipError_t launch_bits(Op op, const StepArgs &a, int32_t n_req, hipStream_t st)
+{
+    if (op == OP_STORE) {
+        const long total = (long)n_req * a.Hc * (a.dk / 4) * (a.dv / 4);
+        const long grid = (total + 255) / 256;
+        hipLaunchKernelGGL((k_store<BITS>), dim3((unsigned)grid), dim3(256), 0, st, a, total);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((long)n_req * a.Hc));
+    if (op == OP_STEP)
+        hipLaunchKernelGGL((k_tile_any<BITS, T, true>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_tile_any<BITS, T, false>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_t(Op op, int bits, const StepArgs &a, int32_t n_req, hipStream_t st)
+{
+    switch (bits) {
+    case 4: return launch_bits<4, T>(op, a, n_req, st);
+    case 6: return launch_bits<6, T>(op, a, n_req, st);
+    case 8: return launch_bits<8, T>(op, a, n_req, st);
+    case 16: return launch_bits<16, T>(op, a, n_req, st);
+    case 32: return launch_bits<32, T>(op, a, n_req, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,
+                          hipStream_t st)
+{
+    if (n_blocks == 0) return hipSuccess;
+    const dim3 grid(n_blocks);
+    if (op == OP_STEP) {
+        if (qkv_bf16)
+            hipLaunchKernelGGL((k_step128<uint16_t, true>), grid, dim3(256), 0, st, f);
+        else
+            hipLaunchKernelGGL((k_step128<float, true>), grid, dim3(256), 0, st, f);
+    } else {
+        if (qkv_bf16)
+            hipLaunchKernelGGL((k_step128<uint16_t, false>), grid, dim3(256), 0, st, f);
+        else
+            hipLaunchKernelGGL((k_step128<float, false>), grid, dim3(256), 0, st, f);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
+                  hipStream_t stream)
+{
+    if (n_req <= 0 || a.Hc <= 0) return hipSuccess;
+    if (qkv_bf16) return launch_t<uint16_t>(op, bits, a, n_req, stream);
+    return launch_t<float>(op, bits, a, n_req, stream);
+}
+
+}  // namespace sqk

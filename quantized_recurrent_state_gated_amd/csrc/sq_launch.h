@@ -1,0 +1,52 @@
+// sq_launch.h -- internal interface between the C-ABI host code (sq_api.hip)
+// and the gfx950 kernels (sq_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqk {
+
+// Everything one launch over one width class needs.  Passed by value.
+struct StepArgs {
+    uint8_t *pool;             // state buffer base
+    uint64_t slab;             // bytes per slot
+    const int64_t *head_off;   // [H] tile offset inside a slab
+    const int32_t *heads;      // [Hc] head ids of this width class
+    int32_t Hc;                // heads in the class
+    int32_t H;                 // heads per request
+    int32_t dk, dv;
+    const int32_t *slot_ids;   // [n_req]
+    const float *rsc;          // [H][dk]
+    const float *csc;          // [H][dv]
+    const void *q, *k, *v;     // [n_req][H][d]
+    const float *alpha, *beta; // [n_req][H]
+    float *o;                  // [n_req][H][dv] or null
+    const float *S;            // store only: [n_req][H][dk][dv]
+};
+
+enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2 };
+
+// One launch over every width class of a d_k = d_v = 128 pool: block b
+// belongs to class c with start[c] <= b < start[c+1]; inside a class the
+// block is request (b - start[c]) / Hc[c], head heads[c][(b - start[c]) % Hc[c]].
+struct FusedArgs {
+    StepArgs a;
+    const int32_t *heads[5];
+    int32_t Hc[5];
+    int32_t bits[5];
+    uint32_t start[5];
+    int32_t n_classes;
+};
+
+// Enqueue `op` for the n_req x Hc tiles of one width class.  bits in
+// {4,6,8,16,32}; qkv_bf16 selects the q/k/v element type.  Returns the HIP
+// error of the launch.
+hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
+                  hipStream_t stream);
+
+// Step or readout over all classes of a d = 128 pool in one launch.
+hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,
+                          hipStream_t stream);
+
+}  // namespace sqk

@@ -1,0 +1,171 @@
+"""Python binding of libsq (include/sq.h): argument marshalling only.
+
+Every function has the name and meaning of the C entry point it wraps.  Device
+buffers are torch tensors on the GPU (PyTorch supplies device memory and
+streams); the arithmetic runs in the library's HIP kernels.  Importing this
+module loads ``libsq.so`` from the package directory and raises if it is
+missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m quantized_recurrent_state_gated_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM = 0, -1, -2, -3, -4
+SQ_F32, SQ_BF16 = 0, 1
+EXPORTED = ("sq_pool_bytes", "sq_pool_alloc", "sq_pool_free", "sq_pool_tile_offset",
+            "sq_pool_store", "sq_decode_step", "sq_readout", "sq_status_string")
+
+
+class SqPoolDesc(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("head_bits", ctypes.POINTER(ctypes.c_uint8)),
+                ("row_scale", ctypes.c_void_p), ("col_scale", ctypes.c_void_p),
+                ("state", ctypes.c_void_p), ("state_bytes", ctypes.c_uint64)]
+
+
+_vp, _i32 = ctypes.c_void_p, ctypes.c_int32
+_lib.sq_pool_bytes.restype = ctypes.c_uint64
+_lib.sq_pool_bytes.argtypes = [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_uint8)]
+_lib.sq_pool_alloc.restype = ctypes.c_int
+_lib.sq_pool_alloc.argtypes = [ctypes.POINTER(SqPoolDesc), ctypes.POINTER(_vp)]
+_lib.sq_pool_free.restype = None
+_lib.sq_pool_free.argtypes = [_vp]
+_lib.sq_pool_tile_offset.restype = ctypes.c_int
+_lib.sq_pool_tile_offset.argtypes = [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_uint64),
+                                     ctypes.POINTER(ctypes.c_uint64)]
+_lib.sq_pool_store.restype = ctypes.c_int
+_lib.sq_pool_store.argtypes = [_vp, _vp, _i32, _vp, _vp]
+_lib.sq_decode_step.restype = ctypes.c_int
+_lib.sq_decode_step.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
+_lib.sq_readout.restype = ctypes.c_int
+_lib.sq_readout.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp]
+_lib.sq_status_string.restype = ctypes.c_char_p
+_lib.sq_status_string.argtypes = [ctypes.c_int]
+
+
+class SqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {sq_status_string(status)} ({status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != SQ_OK:
+        raise SqError(status, where)
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SQ_BF16
+    if t.dtype == torch.float32:
+        return SQ_F32
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _bits_array(head_bits):
+    hb = bytes(int(b) for b in head_bits)
+    return (ctypes.c_uint8 * max(len(hb), 1)).from_buffer_copy(hb or b"\0"), len(hb)
+
+
+def sq_status_string(status: int) -> str:
+    return _lib.sq_status_string(int(status)).decode()
+
+
+def sq_pool_bytes(n_slots: int, n_heads: int, d_k: int, d_v: int, head_bits) -> int:
+    arr, _ = _bits_array(head_bits)
+    return int(_lib.sq_pool_bytes(n_slots, n_heads, d_k, d_v, arr))
+
+
+class SqPool:
+    """Owner of an sq_pool handle; keeps the borrowed tensors alive."""
+
+    def __init__(self, handle: int, keep: tuple, n_slots: int, n_heads: int, d_k: int, d_v: int,
+                 head_bits):
+        self.handle = handle
+        self._keep = keep
+        self.n_slots, self.n_heads, self.d_k, self.d_v = n_slots, n_heads, d_k, d_v
+        self.head_bits = list(int(b) for b in head_bits)
+
+    @property
+    def state(self) -> torch.Tensor:
+        return self._keep[0]
+
+    def __del__(self):
+        sq_pool_free(self)
+
+
+def sq_pool_alloc(n_slots: int, n_heads: int, d_k: int, d_v: int, head_bits, row_scale,
+                  col_scale, state, state_bytes: int | None = None) -> SqPool:
+    """Wrap sq_pool_alloc; `state` is a uint8 device tensor (the caller's buffer)."""
+    arr, nb = _bits_array(head_bits)
+    if state_bytes is None:
+        state_bytes = state.numel() * state.element_size() if hasattr(state, "numel") else 0
+    desc = SqPoolDesc(n_slots, n_heads, d_k, d_v, arr, _ptr(row_scale), _ptr(col_scale),
+                      _ptr(state), int(state_bytes))
+    h = _vp()
+    _check(_lib.sq_pool_alloc(ctypes.byref(desc), ctypes.byref(h)), "sq_pool_alloc")
+    return SqPool(h.value, (state, row_scale, col_scale), n_slots, n_heads, d_k, d_v,
+                  list(head_bits)[:nb])
+
+
+def sq_pool_free(pool: SqPool) -> None:
+    if pool is not None and getattr(pool, "handle", None):
+        _lib.sq_pool_free(pool.handle)
+        pool.handle = None
+
+
+def sq_pool_tile_offset(pool: SqPool, slot: int, head: int):
+    off, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(_lib.sq_pool_tile_offset(pool.handle, slot, head, ctypes.byref(off), ctypes.byref(nb)),
+           "sq_pool_tile_offset")
+    return int(off.value), int(nb.value)
+
+
+def sq_pool_store(pool: SqPool, slot_ids, S, stream=None) -> None:
+    n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    _check(_lib.sq_pool_store(pool.handle, _ptr(slot_ids), n_req, _ptr(S), _stream(stream)),
+           "sq_pool_store")
+
+
+def sq_decode_step(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=None) -> None:
+    n_req = int(slot_ids.numel())
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    _check(_lib.sq_decode_step(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _ptr(k), _ptr(v),
+                               _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream)),
+           "sq_decode_step")
+
+
+def sq_readout(pool: SqPool, slot_ids, q, o, stream=None) -> None:
+    n_req = int(slot_ids.numel())
+    _check(_lib.sq_readout(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _dtype_code(q), _ptr(o),
+                           _stream(stream)), "sq_readout")

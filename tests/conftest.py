@@ -18,3 +18,18 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a visible GPU; elsewhere they are skipped, never faked."""
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

@@ -1,0 +1,138 @@
+"""Helpers shared by the GPU parity tests: field unpacking (written here from
+the state format's definition, independently of both the oracle and the HIP
+library), tolerance checks, and pool set-up.
+
+Tolerances (GPU fp32 arithmetic against the fp64 oracle, teacher-forced: the
+oracle always starts from the GPU's own pre-step bytes):
+  quantized codes  >= 99.99 % identical, every mismatch exactly +-1 code;
+  FP16 pivots      |a - b| <= 1e-3 |b| + 2^-20 max|tile|: the stated 1e-3 relative
+                   bound (one binary16 ulp is <= 2^-10 relative), plus an absolute
+                   floor for elements that come out of cancellation between the
+                   decay term and the key-direction term, whose fp32 evaluation
+                   error is a few fp32 ulps of the tile's magnitude, not of the
+                   (small) result;
+  FP32 states      |a - b| <= 2e-6 * max|tile| (a few fp32 ulps of the tile);
+  readout o        per (request, head): max_j |o - o_ref| <= 1e-5 + 1e-3 max_j |o_ref|.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+CODE_MATCH_MIN = 0.9999
+O_ATOL, O_RTOL = 1e-5, 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def unpack_fields(tiles: np.ndarray, w: int) -> np.ndarray:
+    """tiles: uint8 [n_tiles, tile_bytes] -> uint32 [n_tiles, n_fields], field n at
+    bits [n*w, n*w+w) of each tile's little-endian bit stream."""
+    tiles = np.ascontiguousarray(tiles, np.uint8)
+    nt = tiles.shape[0]
+    if w == 8:
+        return tiles.astype(np.uint32)
+    if w == 16:
+        return tiles.view("<u2").astype(np.uint32).reshape(nt, -1)
+    if w == 32:
+        return tiles.view("<u4").reshape(nt, -1).astype(np.uint32)
+    if w == 4:
+        out = np.empty((nt, tiles.shape[1] * 2), np.uint32)
+        out[:, 0::2] = tiles & 0xF
+        out[:, 1::2] = tiles >> 4
+        return out
+    if w == 6:
+        g = tiles.reshape(nt, -1, 3).astype(np.uint32)
+        word = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+        out = np.stack([(word >> s) & 0x3F for s in (0, 6, 12, 18)], axis=-1)
+        return out.reshape(nt, -1)
+    raise ValueError(w)
+
+
+def f16_order_key(h: np.ndarray) -> np.ndarray:
+    h = h.astype(np.int64)
+    return np.where(h & 0x8000, -(h & 0x7FFF), h)
+
+
+class Tally:
+    """Accumulates code/pivot/fp32/o comparisons over a run."""
+
+    def __init__(self):
+        self.codes = 0
+        self.code_mismatch = 0
+        self.code_maxdiff = 0
+        self.pivot_vals = 0
+        self.pivot_maxulp = 0
+        self.pivot_worst = 0.0  # max of |a-b| / (1e-3 |b| + 2^-20 max|tile|)
+        self.fp32_maxrel = 0.0
+        self.o_worst = 0.0  # max over tiles of err / (atol + rtol * max|o_ref|)
+        self.tiles = 0
+
+    def add_tiles(self, gpu: np.ndarray, ref: np.ndarray, bits: int):
+        """gpu, ref: uint8 [n_tiles, tile_bytes] of one width."""
+        if gpu.shape[0] == 0:
+            return
+        self.tiles += gpu.shape[0]
+        a, b = unpack_fields(gpu, bits), unpack_fields(ref, bits)
+        if bits <= 8:
+            d = np.abs(a.astype(np.int64) - b.astype(np.int64))
+            self.codes += d.size
+            self.code_mismatch += int((d != 0).sum())
+            self.code_maxdiff = max(self.code_maxdiff, int(d.max()))
+        elif bits == 16:
+            d = np.abs(f16_order_key(a) - f16_order_key(b))
+            self.pivot_vals += d.size
+            self.pivot_maxulp = max(self.pivot_maxulp, int(d.max()))
+            fa = a.astype(np.uint16).view(np.float16).astype(np.float64)
+            fb = b.astype(np.uint16).view(np.float16).astype(np.float64)
+            lim = 1e-3 * np.abs(fb) + 2.0 ** -20 * np.abs(fb).max(axis=1, keepdims=True)
+            self.pivot_worst = max(self.pivot_worst, float((np.abs(fa - fb) / lim).max()))
+        else:
+            fa, fb = a.view(np.float32), b.view(np.float32)
+            scale = np.maximum(np.abs(fb).max(axis=1, keepdims=True), 1e-30)
+            self.fp32_maxrel = max(self.fp32_maxrel, float((np.abs(fa - fb) / scale).max()))
+
+    def add_o(self, o_gpu: np.ndarray, o_ref: np.ndarray):
+        """o arrays [..., dv]."""
+        err = np.abs(o_gpu - o_ref).max(axis=-1)
+        lim = O_ATOL + O_RTOL * np.abs(o_ref).max(axis=-1)
+        self.o_worst = max(self.o_worst, float((err / lim).max()))
+
+    def match_rate(self) -> float:
+        return 1.0 - self.code_mismatch / self.codes if self.codes else 1.0
+
+    def summary(self) -> str:
+        return (f"tiles={self.tiles} codes={self.codes} mismatch={self.code_mismatch} "
+                f"(match {100 * self.match_rate():.5f}%) maxdiff={self.code_maxdiff} "
+                f"pivot_maxulp={self.pivot_maxulp} pivot_worst={self.pivot_worst:.3f} fp32_maxrel={self.fp32_maxrel:.2e} "
+                f"o_worst={self.o_worst:.3f}")
+
+    def check(self):
+        assert self.code_maxdiff <= 1, self.summary()
+        assert self.match_rate() >= CODE_MATCH_MIN, self.summary()
+        assert self.pivot_worst <= 1.0, self.summary()
+        assert self.fp32_maxrel <= 2e-6, self.summary()
+        assert self.o_worst <= 1.0, self.summary()
+
+
+def compare_pools(tally: Tally, gpu_pool: np.ndarray, ref_pool: np.ndarray, head_bits, off, slab,
+                  slots, dk, dv):
+    """Compare the tiles of `slots` (all heads) of two host pool images."""
+    head_bits = np.asarray(head_bits)
+    for b in sorted(set(int(x) for x in head_bits)):
+        hs = np.nonzero(head_bits == b)[0]
+        tb = dk * dv * b // 8
+        idx = np.array([p * slab + off[h] for p in slots for h in hs], np.int64)
+        if idx.size == 0:
+            continue
+        sel = idx[:, None] + np.arange(tb)[None, :]
+        tally.add_tiles(gpu_pool[sel], ref_pool[sel], b)
+
+
+def host_f32(x: torch.Tensor) -> np.ndarray:
+    return x.detach().float().cpu().numpy()

@@ -1,0 +1,86 @@
+"""The C-ABI library: it loads, exports every entry point include/sq.h
+declares, computes pool sizes as the state format defines them, and rejects
+bad arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sq.h")
+
+
+@pytest.fixture(scope="module")
+def sq():
+    from quantized_recurrent_state_gated_amd import sq as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names(sq):
+    assert _declared() == sorted(sq.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(sq):
+    lib = ctypes.CDLL(sq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_pool_bytes_matches_state_format(sq, orc):
+    for bits, dk, dv in [([4, 6, 8, 16, 32], 128, 128), ([8] * 4, 16, 16), ([6, 4], 12, 20),
+                         ([4], 4, 4), ([16, 6], 256, 128)]:
+        _, slab = orc.pool_layout(bits, dk, dv)
+        assert sq.sq_pool_bytes(3, len(bits), dk, dv, bits) == 3 * slab
+    # serving shape: 70 x 2304 heads at 568/1136/568 + 32 pivots
+    bits = [4] * 568 + [6] * 1136 + [8] * 568 + [16] * 32
+    assert sq.sq_pool_bytes(70, 2304, 128, 128, bits) == 2027683840
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1, 16, 16, [8]), (1, 0, 16, 16, []), (1, 1, 16, 16, [5]), (1, 1, 16, 16, [12]),
+    (1, 1, 18, 16, [8]), (1, 1, 16, 0, [8]), (1, 1, 512, 16, [8]), (1, 2, 16, 16, [8, 7]),
+])
+def test_pool_bytes_rejects_bad_shapes(sq, args):
+    assert sq.sq_pool_bytes(*args) == 0
+
+
+def _desc(sq, **kw):
+    bits = kw.pop("bits", [8, 4])
+    arr = (ctypes.c_uint8 * len(bits))(*bits)
+    d = dict(n_slots=2, n_heads=len(bits), d_k=16, d_v=16, head_bits=arr, row_scale=0x10000,
+             col_scale=0x20000, state=0x100000, state_bytes=1 << 20)
+    d.update(kw)
+    return sq.SqPoolDesc(**d), arr
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_slots=0), -1), (dict(n_heads=0), -1), (dict(state=None), -1), (dict(state=0x100010), -1),
+    (dict(row_scale=None), -1), (dict(col_scale=0x20004), -1), (dict(state_bytes=100), -1),
+    (dict(bits=[8, 3]), -2), (dict(d_k=18), -2), (dict(d_v=260), -2),
+])
+def test_pool_alloc_validates_before_any_hip_call(sq, kw, status):
+    desc, keep = _desc(sq, **kw)
+    h = ctypes.c_void_p()
+    assert sq._lib.sq_pool_alloc(ctypes.byref(desc), ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_null_handles_and_status_strings(sq):
+    assert sq._lib.sq_pool_alloc(None, None) == sq.SQ_ERR_INVALID
+    sq._lib.sq_pool_free(None)
+    assert sq._lib.sq_decode_step(None, None, 1, None, None, None, 0, None, None, None, None) == -1
+    assert sq._lib.sq_readout(None, None, 1, None, 0, None, None) == -1
+    assert sq._lib.sq_pool_store(None, None, 1, None, None) == -1
+    off = ctypes.c_uint64()
+    assert sq._lib.sq_pool_tile_offset(None, 0, 0, ctypes.byref(off), ctypes.byref(off)) == -1
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(sq.sq_status_string(s), str) and sq.sq_status_string(s)
+    assert sq.sq_status_string(-2) != sq.sq_status_string(-1)

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every step is teacher-forced: the oracle starts from the GPU's own pre-step
+bytes with identical inputs, and the two post-step states and readouts are
+compared to the tolerances in gpu_harness.  Sizes here span several tiles and
+every width class; the full-size workloads are in test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import Tally, compare_pools, host_f32, say, unpack_fields
+from quantized_recurrent_state_gated_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_THREADS = 16
+
+
+@pytest.fixture(scope="module")
+def sq():
+    from quantized_recurrent_state_gated_amd import sq as m
+    return m
+
+
+class Case:
+    """A pool on the GPU initialised from the oracle's quantize-and-store."""
+
+    def __init__(self, sq, orc, w, n_slots=None, slots=None, bits=None, scales=None, S0=None):
+        self.sq, self.orc, self.w = sq, orc, w
+        self.bits = np.asarray(I.head_bits(w) if bits is None else bits, np.uint8)
+        H, dk, dv = w.n_heads, w.dk, w.dv
+        if scales is None:
+            r, c = I.scales(w)
+            r, c = r.numpy(), c.numpy()
+        else:
+            r, c = scales
+        self.r, self.c = np.ascontiguousarray(r, np.float32), np.ascontiguousarray(c, np.float32)
+        self.off, self.slab = orc.pool_layout(self.bits, dk, dv)
+        self.n_slots = n_slots or w.n_req
+        self.slots = np.arange(w.n_req, dtype=np.int32) if slots is None else np.asarray(slots, np.int32)
+        host = np.zeros(self.n_slots * self.slab, np.uint8)
+        if S0 is None:
+            S0 = torch.stack([I.initial_state(w, p) for p in range(w.n_req)]).numpy()
+        self.S0 = np.ascontiguousarray(S0, np.float32)
+        orc.store_pool(host, self.bits, dk, dv, self.r, self.c, self.slots, self.S0)
+        self.dev = torch.from_numpy(host).cuda()
+        self.rd = torch.from_numpy(self.r).cuda()
+        self.cd = torch.from_numpy(self.c).cuda()
+        self.pool = sq.sq_pool_alloc(self.n_slots, H, dk, dv, self.bits, self.rd, self.cd, self.dev)
+        self.slots_d = torch.from_numpy(self.slots).cuda()
+
+    def host(self):
+        torch.cuda.synchronize()
+        return self.dev.cpu().numpy()
+
+    def step(self, si, want_o=True):
+        w = self.w
+        o = torch.empty(w.n_req, w.n_heads, w.dv, device="cuda") if want_o else None
+        self.sq.sq_decode_step(self.pool, self.slots_d, si.q.cuda(), si.k.cuda(), si.v.cuda(),
+                               si.alpha.cuda(), si.beta.cuda(), o)
+        return o
+
+    def oracle_step(self, pre, si):
+        ref = pre.copy()
+        o = self.orc.step_pool(ref, self.bits, self.w.dk, self.w.dv, self.r, self.c, self.slots,
+                               host_f32(si.q), host_f32(si.k), host_f32(si.v), host_f32(si.alpha),
+                               host_f32(si.beta), n_threads=ORACLE_THREADS)
+        return ref, o
+
+    def compare(self, tally, post, ref):
+        compare_pools(tally, post, ref, self.bits, self.off, self.slab, self.slots, self.w.dk,
+                      self.w.dv)
+
+
+def run_teacher_forced(case, steps, label, check_changes=True):
+    tally = Tally()
+    changed = 0
+    for t in range(steps):
+        si = I.step_inputs(case.w, t)
+        pre = case.host()
+        o = case.step(si)
+        post = case.host()
+        ref, o_ref = case.oracle_step(pre, si)
+        case.compare(tally, post, ref)
+        tally.add_o(o.cpu().numpy(), o_ref)
+        changed += int((post != pre).any())
+        if t % 32 == 0 or t == steps - 1:
+            say(f"[{label}] step {t}: {tally.summary()}")
+    tally.check()
+    if check_changes:
+        assert changed == steps  # every step moved the state
+    return tally
+
+
+# ------------------------------------------------------------------ store
+
+@pytest.mark.parametrize("name,shape", [("tiny", None), ("layer", (3, 12)), ("any", (2, 5))])
+def test_store_bit_exact(sq, orc, name, shape):
+    if name == "any":
+        w = I.Workload("any", 2, 5, 12, 20, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=77)
+    else:
+        w = I.WORKLOADS[name] if shape is None else I.scaled(I.WORKLOADS[name], *shape)
+    say(f"store {w.name} {w.n_req}x{w.n_heads} d={w.dk}x{w.dv}")
+    case = Case(sq, orc, w, n_slots=w.n_req + 1, slots=np.arange(w.n_req)[::-1] + 1)
+    ref = case.host()
+    case.dev.zero_()
+    S0 = torch.from_numpy(case.S0).cuda()
+    sq.sq_pool_store(case.pool, case.slots_d, S0)
+    got = case.host()
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ step parity
+
+def test_tiny_all_steps(sq, orc):
+    w = I.WORKLOADS["tiny"]
+    run_teacher_forced(Case(sq, orc, w), w.steps, "tiny")
+
+
+def test_tiny_literal_scales_degenerate(sq, orc):
+    """The tiny recipe's column factors read literally as steps (0.5..2): an
+    N(0, 0.1^2) state then quantizes to all-zero codes; the step must still
+    agree with the oracle (codes move only where updates exceed half a step)."""
+    w = I.WORKLOADS["tiny"]
+    r, c = I.scales(w)
+    case = Case(sq, orc, w, scales=(r.numpy(), c.numpy() * 127.0))
+    pre = case.host()
+    fields = unpack_fields(pre[None, : orc.tile_bytes(8, 16, 16)], 8)
+    assert np.all(fields == 128)  # every code is zero
+    run_teacher_forced(case, w.steps, "tiny-literal", check_changes=False)
+
+
+def test_layer_all_steps(sq, orc):
+    w = I.WORKLOADS["layer"]
+    run_teacher_forced(Case(sq, orc, w), w.steps, "layer")
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_d128_every_width(sq, orc, qkv):
+    w = I.Workload("mix", 3, 10, 128, 128, 4, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, qkv_dtype=qkv,
+                   seed=99)
+    run_teacher_forced(Case(sq, orc, w, n_slots=5, slots=[4, 1, 2]), w.steps, f"mix-{qkv}")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (12, 20), (128, 64), (64, 128), (256, 32), (4, 4)])
+def test_other_shapes(sq, orc, dk, dv):
+    w = I.Workload("shape", 2, 5, dk, dv, 3, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=dk * 1000 + dv)
+    run_teacher_forced(Case(sq, orc, w), w.steps, f"shape{dk}x{dv}")
+
+
+def test_single_width_pools(sq, orc):
+    for bits in (4, 6, 8, 16, 32):
+        w = I.Workload(f"only{bits}", 2, 3, 128, 128, 2, {bits: 3}, seed=bits)
+        run_teacher_forced(Case(sq, orc, w), w.steps, w.name)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+def test_pure_decay_keeps_codes_and_readout(sq, orc):
+    """beta = 0, alpha = 1: codes are unchanged bit for bit, o = S^T q equals
+    sq_readout, for every width."""
+    w = I.Workload("decay", 2, 10, 128, 128, 3, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, seed=5)
+    case = Case(sq, orc, w)
+    start = case.host()
+    for t in range(w.steps):
+        si = I.step_inputs(w, t)
+        si.alpha.fill_(1.0)
+        si.beta.zero_()
+        o = case.step(si)
+        assert np.array_equal(case.host(), start)
+        o2 = torch.empty_like(o)
+        sq.sq_readout(case.pool, case.slots_d, si.q.cuda(), o2)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(o.cpu().numpy(), o2.cpu().numpy(), rtol=1e-6, atol=1e-6)
+        o_ref = orc.readout_pool(start, case.bits, w.dk, w.dv, case.r, case.c, case.slots,
+                                 host_f32(si.q))
+        t2 = Tally()
+        t2.add_o(o2.cpu().numpy(), o_ref)
+        t2.check()
+
+
+def test_write_into_row(sq, orc):
+    """alpha = beta = 1, k = e_m: only row m changes."""
+    w = I.Workload("row", 1, 5, 128, 128, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=6)
+    case = Case(sq, orc, w)
+    pre = case.host()
+    si = I.step_inputs(w, 0)
+    m = 37
+    si.alpha.fill_(1.0)
+    si.beta.fill_(1.0)
+    k = torch.zeros_like(si.k)
+    k[..., m] = 1.0
+    si.k = k
+    case.step(si)
+    post = case.host()
+    for h in range(w.n_heads):
+        b = int(case.bits[h])
+        tb = orc.tile_bytes(b, 128, 128)
+        lo = int(case.off[h])
+        S_pre = orc.decode_tile(b, 128, 128, pre[lo:lo + tb], case.r[h], case.c[h])
+        S_post = orc.decode_tile(b, 128, 128, post[lo:lo + tb], case.r[h], case.c[h])
+        others = np.arange(128) != m
+        assert np.array_equal(S_post[others], S_pre[others])
+        assert not np.array_equal(S_post[m], S_pre[m])
+    ref, _ = case.oracle_step(pre, si)
+    tally = Tally()
+    case.compare(tally, post, ref)
+    tally.check()
+
+
+def test_determinism_and_checkpoint_restore(sq, orc):
+    """Two runs from one snapshot are bit-identical (no atomics, fixed order);
+    restoring the snapshot and replaying reproduces pool and readouts."""
+    w = I.scaled(I.WORKLOADS["layer"], 4, 24, 6)
+    case = Case(sq, orc, w)
+    for t in range(2):
+        case.step(I.step_inputs(w, t))
+    snap = case.dev.clone()
+    runs = []
+    for _ in range(2):
+        case.dev.copy_(snap)
+        outs = [case.step(I.step_inputs(w, t)).cpu() for t in range(2, w.steps)]
+        runs.append((case.host().copy(), outs))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    for a, b in zip(runs[0][1], runs[1][1]):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_batch_is_noop(sq, orc):
+    w = I.scaled(I.WORKLOADS["layer"], 2, 6, 1)
+    case = Case(sq, orc, w)
+    pre = case.host()
+    empty = torch.zeros(0, dtype=torch.int32, device="cuda")
+    z = torch.zeros(0, device="cuda")
+    sq.sq_decode_step(case.pool, empty, z, z, z, z, z, None)
+    sq.sq_readout(case.pool, empty, z, z)
+    sq.sq_pool_store(case.pool, empty, z)
+    assert np.array_equal(case.host(), pre)
+
+
+def test_subset_of_slots_and_no_readout(sq, orc):
+    """A batch touching 3 of 7 slots in scrambled order, o not requested:
+    untouched slots keep their bytes."""
+    w = I.scaled(I.WORKLOADS["layer"], 3, 12, 2)
+    case = Case(sq, orc, w, n_slots=7, slots=[6, 2, 4])
+    for t in range(w.steps):
+        si = I.step_inputs(w, t)
+        pre = case.host()
+        case.step(si, want_o=False)
+        post = case.host()
+        for p in (0, 1, 3, 5):
+            assert np.array_equal(post[p * case.slab:(p + 1) * case.slab],
+                                  pre[p * case.slab:(p + 1) * case.slab])
+        ref, _ = case.oracle_step(pre, si)
+        tally = Tally()
+        case.compare(tally, post, ref)
+        tally.check()
+
+
+def test_host_errors_with_a_live_pool(sq, orc):
+    w = I.scaled(I.WORKLOADS["layer"], 2, 6, 1)
+    case = Case(sq, orc, w)
+    si = I.step_inputs(w, 0)
+    q, k, v = si.q.cuda(), si.k.cuda(), si.v.cuda()
+    a, b = si.alpha.cuda(), si.beta.cuda()
+    with pytest.raises(sq.SqError) as e:
+        too_many = torch.zeros(3, dtype=torch.int32, device="cuda")
+        sq.sq_decode_step(case.pool, too_many, q, k, v, a, b)
+    assert e.value.status == sq.SQ_ERR_INVALID
+    with pytest.raises(sq.SqError):
+        rc = sq._lib.sq_decode_step(case.pool.handle, case.slots_d.data_ptr(), 2, q.data_ptr() + 2,
+                                    k.data_ptr(), v.data_ptr(), 1, a.data_ptr(), b.data_ptr(),
+                                    None, None)
+        sq._check(rc, "misaligned q")
+    assert sq._lib.sq_decode_step(case.pool.handle, case.slots_d.data_ptr(), 2, q.data_ptr(),
+                                  k.data_ptr(), v.data_ptr(), 7, a.data_ptr(), b.data_ptr(), None,
+                                  None) == sq.SQ_ERR_INVALID
+    off, nb = sq.sq_pool_tile_offset(case.pool, 1, 3)
+    assert off == case.slab + int(case.off[3]) and nb == orc.tile_bytes(int(case.bits[3]), 128, 128)
+    with pytest.raises(sq.SqError):
+        sq.sq_pool_tile_offset(case.pool, 2, 0)
