@@ -63,6 +63,54 @@ def traffic_from_profile(sha: str):
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30  # the calibration copy of --copy-calibration
+
+
+def _pmc_rows(path, counter):
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    step = [float(r["Counter_Value"]) * 1024 for r in rows if "k_step128" in r["Kernel_Name"]]
+    copies = [float(r["Counter_Value"]) * 1024 for r in rows
+              if "copyBuffer" in r["Kernel_Name"] or "copy_kernel" in r["Kernel_Name"]]
+    return step, copies
+
+
+def pmc_summary(fetch_csv: str, write_csv: str) -> int:
+    """HBM bytes per step launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by the factor that makes the same counter read the known size
+    of the 1 GiB calibration copy."""
+    import statistics
+    fs, fc = _pmc_rows(fetch_csv, "FETCH_SIZE")
+    ws, wc = _pmc_rows(write_csv, "WRITE_SIZE")
+    ff = COPY_BYTES / max(fc)
+    fw = COPY_BYTES / max(wc)
+    fetch = statistics.median(fs) * ff
+    write = statistics.median(ws) * fw
+    out = {"kernel_source_sha": kernel_source_sha(), "fetch_bytes_per_launch": fetch,
+           "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
+           "fetch_factor": ff, "write_factor": fw, "dispatches": [len(fs), len(ws)],
+           "raw_fetch_kib": statistics.median(fs) / 1024, "raw_write_kib": statistics.median(ws) / 1024,
+           "calibration": "1 GiB device copy (hipMemcpy D2D blit kernel): FETCH_SIZE and WRITE_SIZE "
+                          "each scaled so that it reads 1 GiB",
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o <name> -- python3 "
+                        f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def trace_summary(stats_csv: str) -> int:
+    import csv
+    for r in csv.DictReader(open(stats_csv)):
+        if "k_step128" in r["Name"]:
+            print(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} |")
+    return 0
+
+
 def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
     """The oracle, as it stands, on a bounded sample: whole requests (all 2304
     heads) of the same workload, calibrated to about target_s seconds."""
@@ -106,7 +154,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-calibration` into profiles/ and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                    help="print the step kernel's row of a rocprofv3 --stats csv and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -167,16 +224,18 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events around every launch, on the stream the kernel runs on
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for t in range(args.steps):
         step(args.warmup + t)
-    ev1.record(stream)
+        evs[t + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    gpu_ms = ev0.elapsed_time(ev1)
+    per = sorted(evs[t].elapsed_time(evs[t + 1]) for t in range(args.steps))
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / args.steps
     log(f"[bench] {args.steps} timed steps: {gpu_ms:.3f} ms events, {wall * 1e3:.3f} ms wall")
 
@@ -220,6 +279,7 @@ def main() -> int:
             "kernel": "k_step128 (one launch = one decode step over all tiles)",
             "algorithmic_bytes_per_launch": bpstep,
             "avg_launch_ms": ms_per_step,
+            "launch_ms_min_median_max": [per[0], per[len(per) // 2], per[-1]],
             "kernel_source_sha": sha,
         },
         "cpu_baseline": None,

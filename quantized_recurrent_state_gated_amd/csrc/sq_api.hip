@@ -69,8 +69,9 @@ struct sq_pool {
     uint8_t *state;
     uint64_t state_bytes;
     int device;
-    void *dtab;               // device: int64 head_off[H] | int32 heads grouped by class
+    void *dtab;               // device: int64 head_off[H] | int32 heads grouped by class | u8 bits[H]
     int64_t *d_off;
+    uint8_t *d_bits;
     int32_t *d_heads[5];
     int32_t n_class[5];
 };
@@ -117,7 +118,7 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
 
     // host image of the device table: offsets, then head ids grouped by width
     const size_t H = (size_t)d.n_heads;
-    std::vector<unsigned char> img(H * 8 + H * 4);
+    std::vector<unsigned char> img(H * 8 + H * 4 + H);
     memcpy(img.data(), off.data(), H * 8);
     int32_t *heads = reinterpret_cast<int32_t *>(img.data() + H * 8);
     size_t pos = 0;
@@ -131,6 +132,7 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
                 p->n_class[c]++;
             }
     }
+    memcpy(img.data() + H * 12, d.head_bits, H);
     if (hipGetDevice(&p->device) != hipSuccess) {
         delete p;
         return SQ_ERR_HIP;
@@ -147,6 +149,7 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     p->d_off = static_cast<int64_t *>(p->dtab);
     int32_t *dheads = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(p->dtab) + H * 8);
     for (int c = 0; c < 5; c++) p->d_heads[c] = dheads + start[c];
+    p->d_bits = static_cast<unsigned char *>(p->dtab) + H * 12;
     *out = p;
     return SQ_OK;
 }
@@ -188,24 +191,15 @@ static sqk::StepArgs base_args(const sq_pool *p, const int32_t *slot_ids)
 static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16, int32_t n_req,
                        void *stream)
 {
-    // heaviest tiles first: FP32, FP16 pivots, then 8-, 6- and 4-bit heads
+    // d = 128: one launch over all tiles in pool order; otherwise one launch
+    // per width class, widest tiles first
     static const int order[5] = {4, 3, 2, 1, 0};
     if (op != sqk::OP_STORE && p->dk == 128 && p->dv == 128) {
-        sqk::FusedArgs f;
-        memset(&f, 0, sizeof(f));
-        f.a = a;
-        uint64_t total = 0;
-        for (int oc = 0; oc < 5; oc++) {
-            const int c = order[oc];
-            if (p->n_class[c] == 0) continue;
-            const int i = f.n_classes++;
-            f.heads[i] = p->d_heads[c];
-            f.Hc[i] = p->n_class[c];
-            f.bits[i] = kClasses[c];
-            f.start[i] = (uint32_t)total;
-            total += (uint64_t)n_req * (uint64_t)p->n_class[c];
-        }
+        const uint64_t total = (uint64_t)n_req * (uint64_t)p->n_heads;
         if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
+        sqk::FusedArgs f;
+        f.a = a;
+        f.head_bits = p->d_bits;
         if (sqk::launch_fused128(op, bf16, f, (uint32_t)total, (hipStream_t)stream) != hipSuccess)
             return SQ_ERR_HIP;
         return SQ_OK;

@@ -81,10 +81,12 @@ __device__ __forceinline__ void decode(const uint32_t (&d)[BITS / 2], float (&f)
         for (int e = 0; e < 16; e++) f[e] = (float)((d[e >> 2] >> (8 * (e & 3))) & 0xffu);
     } else if constexpr (BITS == 4) {
         // split each dword's nibbles into two dwords of bytes, then convert
-        // bytes directly (v_cvt_f32_ubyte0..3)
+        // bytes directly (v_cvt_f32_ubyte0..3); the empty asm keeps the
+        // compiler from folding the masks back into per-field bit extracts
 #pragma unroll
         for (int w = 0; w < 2; w++) {
-            const uint32_t lo = d[w] & 0x0f0f0f0fu, hi = (d[w] >> 4) & 0x0f0f0f0fu;
+            uint32_t lo = d[w] & 0x0f0f0f0fu, hi = (d[w] >> 4) & 0x0f0f0f0fu;
+            asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
             for (int p = 0; p < 4; p++) {
                 f[8 * w + 2 * p] = (float)((lo >> (8 * p)) & 0xffu);
@@ -153,8 +155,10 @@ __device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[BITS 
             d[w] = ev | (od << 4);
         }
     } else if constexpr (BITS == 6) {
-        // four codes of a column -> four bytes -> one 24-bit group, then the
-        // four groups are spliced into three dwords
+        // four codes of a column -> four bytes (each < 64) -> one 24-bit group
+        // f0 | f1 << 6 | f2 << 12 | f3 << 18, as two byte dot products
+        // (f0 + 64 f1 and f2 + 64 f3) joined by a shift-or; the four 3-byte
+        // groups are then spliced into three dwords with byte permutes
         uint32_t g[4];
 #pragma unroll
         for (int c = 0; c < 4; c++) {
@@ -162,13 +166,13 @@ __device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[BITS 
             x = pk_u8(clamp_code<6>(z[4 * c + 1]), 1, x);
             x = pk_u8(clamp_code<6>(z[4 * c + 2]), 2, x);
             x = pk_u8(clamp_code<6>(z[4 * c + 3]), 3, x);
-            // bytes are < 64: pair them into 12-bit halves, then join the halves
-            const uint32_t a = (x & 0x003f003fu) | ((x >> 2) & 0x0fc00fc0u);
-            g[c] = __builtin_amdgcn_ubfe(a, 0, 12) | ((a >> 4) & 0x00fff000u);
+            const uint32_t lo12 = __builtin_amdgcn_udot4(x, 0x00004001u, 0u, false);
+            const uint32_t hi12 = __builtin_amdgcn_udot4(x, 0x40010000u, 0u, false);
+            g[c] = lo12 | (hi12 << 12);
         }
-        d[0] = g[0] | (g[1] << 24);
-        d[1] = (g[1] >> 8) | (g[2] << 16);
-        d[2] = (g[2] >> 16) | (g[3] << 8);
+        d[0] = __builtin_amdgcn_perm(g[1], g[0], 0x04020100u);  // g0 bytes 0-2, g1 byte 0
+        d[1] = __builtin_amdgcn_perm(g[2], g[1], 0x05040201u);  // g1 bytes 1-2, g2 bytes 0-1
+        d[2] = __builtin_amdgcn_perm(g[3], g[2], 0x06050402u);  // g2 byte 2, g3 bytes 0-2
     } else if constexpr (BITS == 16) {
 #pragma unroll
         for (int w = 0; w < 8; w++) {
@@ -182,44 +186,74 @@ __device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[BITS 
     }
 }
 
-template <int BITS>
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Tile blocks are streamed: read once, written once, never reused by this
+// launch, so they may bypass cache retention (nontemporal hint).
+template <int BITS, bool NT>
 __device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[BITS / 2])
 {
     if constexpr (BITS == 4) {
-        uint2 x = *reinterpret_cast<const uint2 *>(p);
+        const u32x2 *q = reinterpret_cast<const u32x2 *>(p);
+        const u32x2 x = NT ? __builtin_nontemporal_load(q) : *q;
         d[0] = x.x; d[1] = x.y;
     } else if constexpr (BITS == 6) {
         const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-        d[0] = q[0]; d[1] = q[1]; d[2] = q[2];
+#pragma unroll
+        for (int w = 0; w < 3; w++) d[w] = NT ? __builtin_nontemporal_load(q + w) : q[w];
     } else {
 #pragma unroll
         for (int w = 0; w < BITS / 2; w += 4) {
-            uint4 x = *reinterpret_cast<const uint4 *>(p + 4 * w);
+            const u32x4 *q = reinterpret_cast<const u32x4 *>(p + 4 * w);
+            const u32x4 x = NT ? __builtin_nontemporal_load(q) : *q;
             d[w] = x.x; d[w + 1] = x.y; d[w + 2] = x.z; d[w + 3] = x.w;
         }
     }
 }
 
-template <int BITS>
+template <int BITS, bool NT>
 __device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[BITS / 2])
 {
     if constexpr (BITS == 4) {
-        *reinterpret_cast<uint2 *>(p) = make_uint2(d[0], d[1]);
+        u32x2 *q = reinterpret_cast<u32x2 *>(p);
+        const u32x2 x = {d[0], d[1]};
+        if (NT) __builtin_nontemporal_store(x, q); else *q = x;
     } else if constexpr (BITS == 6) {
         uint32_t *q = reinterpret_cast<uint32_t *>(p);
-        q[0] = d[0]; q[1] = d[1]; q[2] = d[2];
+#pragma unroll
+        for (int w = 0; w < 3; w++) {
+            if (NT) __builtin_nontemporal_store(d[w], q + w); else q[w] = d[w];
+        }
     } else {
 #pragma unroll
-        for (int w = 0; w < BITS / 2; w += 4)
-            *reinterpret_cast<uint4 *>(p + 4 * w) = make_uint4(d[w], d[w + 1], d[w + 2], d[w + 3]);
+        for (int w = 0; w < BITS / 2; w += 4) {
+            u32x4 *q = reinterpret_cast<u32x4 *>(p + 4 * w);
+            const u32x4 x = {d[w], d[w + 1], d[w + 2], d[w + 3]};
+            if (NT) __builtin_nontemporal_store(x, q); else *q = x;
+        }
     }
+}
+
+// Sum over the 64 lanes of a wave with DPP row operations; the total is
+// returned in every lane (read back from lane 63).
+__device__ __forceinline__ float dpp_add(float x, float y) { return x + y; }
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
 }
 
 __device__ __forceinline__ float wave_sum(float x)
 {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s, 64);
-    return x;
+    x += dpp<0xb1>(x);        // quad_perm [1,0,3,2]
+    x += dpp<0x4e>(x);        // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);       // row_half_mirror: sums of 8
+    x += dpp<0x140>(x);       // row_mirror: sums of 16
+    x += dpp<0x142, 0xa>(x);  // row_bcast15 into rows 1, 3: sums of 32 there
+    x += dpp<0x143, 0xc>(x);  // row_bcast31 into rows 2, 3: lane 63 holds the total
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // ---------------------------------------------------------------- d = 128 step
@@ -235,8 +269,8 @@ __device__ __forceinline__ float wave_sum(float x)
 
 struct Smem128 {
     float w[128], g[128], a[128];  // per-row factors k_i r_i, q_i r_i, beta k_i / r_i
-    float red[8][8][32];           // [row group][u0..u3, y0..y3][column block]
-    float tot[8][32];
+    alignas(16) float red[8][2][128];  // [row group][u, y][column] partial sums
+    alignas(16) float b[128];      // per-column (v_j - alpha u_j) / c_j
     float sum[2][3];               // per-wave partials of q.k, sum w, sum g
 };
 
@@ -247,6 +281,9 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
     constexpr int BLK_BYTES = 2 * BITS;
+    // code tiles stream with the nontemporal hint (measured faster on gfx950);
+    // FP16/FP32 tiles measured faster without it
+    constexpr bool NT = QUANT;
 
     const int t = threadIdx.x;
     const int cb = t & 31, rg = t >> 5;
@@ -260,7 +297,7 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
     // the tile: 4 blocks per thread, issued first
     uint32_t d[4][W];
 #pragma unroll
-    for (int m = 0; m < 4; m++) load_block<BITS>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
+    for (int m = 0; m < 4; m++) load_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
 
     const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
     const float beta = UPDATE ? a.beta[nh] : 0.0f;
@@ -281,10 +318,6 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
             sm.sum[t >> 6][2] = s2;
         }
     }
-    float cc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (QUANT) ld4<float>(a.csc, (long)h * 128 + 4 * cb, cc);
-    float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (UPDATE) ld4<T>(v, nh * 128 + 4 * cb, vv);
     __syncthreads();
 
     // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
@@ -305,43 +338,36 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
             }
         }
     }
-#pragma unroll
-    for (int cj = 0; cj < 4; cj++) {
-        sm.red[rg][cj][cb] = pu[cj];
-        sm.red[rg][4 + cj][cb] = py[cj];
-    }
-    __syncthreads();
-    {
-        const int e = t >> 5, c2 = t & 31;
-        float s = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 8; r++) s += sm.red[r][e][c2];
-        sm.tot[e][c2] = s;
-    }
+    *reinterpret_cast<float4 *>(&sm.red[rg][0][4 * cb]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
+    *reinterpret_cast<float4 *>(&sm.red[rg][1][4 * cb]) = make_float4(py[0], py[1], py[2], py[3]);
     __syncthreads();
 
-    const float qk = sm.sum[0][0] + sm.sum[1][0];
-    const float Wsum = sm.sum[0][1] + sm.sum[1][1];
-    const float Gsum = sm.sum[0][2] + sm.sum[1][2];
-    float u[4], y[4];
+    // column finalisation: thread j < 128 owns column j
+    if (t < 128) {
+        float U = 0.0f, Y = 0.0f;
 #pragma unroll
-    for (int cj = 0; cj < 4; cj++) {
-        u[cj] = cc[cj] * (sm.tot[cj][cb] - OFF * Wsum);
-        y[cj] = cc[cj] * (sm.tot[4 + cj][cb] - OFF * Gsum);
+        for (int r = 0; r < 8; r++) {
+            U += sm.red[r][0][t];
+            Y += sm.red[r][1][t];
+        }
+        const float qk = sm.sum[0][0] + sm.sum[1][0];
+        const float Wsum = sm.sum[0][1] + sm.sum[1][1];
+        const float Gsum = sm.sum[0][2] + sm.sum[1][2];
+        const float cjs = QUANT ? a.csc[(long)h * 128 + t] : 1.0f;
+        const float uj = cjs * (U - OFF * Wsum);
+        const float yj = cjs * (Y - OFF * Gsum);
+        if (!UPDATE) {
+            a.o[nh * 128 + t] = yj;
+        } else {
+            const float e = ld1(v, nh * 128 + t) - alpha * uj;
+            if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * qk * e);
+            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cjs) : e;
+        }
     }
-    float *o = a.o ? a.o + nh * 128 + 4 * cb : nullptr;
-    if (!UPDATE) {
-        if (rg == 0) *reinterpret_cast<float4 *>(o) = make_float4(y[0], y[1], y[2], y[3]);
-        return;
-    }
-    float b[4], ov[4];
-#pragma unroll
-    for (int cj = 0; cj < 4; cj++) {
-        const float e = vv[cj] - alpha * u[cj];
-        ov[cj] = fmaf(alpha, y[cj], beta * qk * e);
-        b[cj] = QUANT ? e * __builtin_amdgcn_rcpf(cc[cj]) : e;
-    }
-    if (o && rg == 0) *reinterpret_cast<float4 *>(o) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    if (!UPDATE) return;
+    __syncthreads();
+    const float4 b4 = *reinterpret_cast<const float4 *>(&sm.b[4 * cb]);
+    const float b[4] = {b4.x, b4.y, b4.z, b4.w};
 
     // pass 2: z = alpha n + a_i b_j + OFF (1 - alpha), requantize, repack, store
     const float C = OFF * (1.0f - alpha);
@@ -358,23 +384,21 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
         }
         uint32_t dn[W];
         encode<BITS>(z, dn);
-        store_block<BITS>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, dn);
+        store_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, dn);
     }
 }
 
 template <typename T, bool UPDATE>
 __global__ __launch_bounds__(256) void k_step128(FusedArgs f)
 {
+    // block b is request b / H, head b % H: the grid walks the pool in memory
+    // order, so tiles of every width are interleaved on each CU (VALU-heavy
+    // narrow codes overlap with memory-heavy wide tiles)
     __shared__ Smem128 sm;
     const uint32_t b = blockIdx.x;
-    int c = 0;
-#pragma unroll
-    for (int i = 1; i < 5; i++)
-        if (i < f.n_classes && b >= f.start[i]) c = i;
-    const uint32_t local = b - f.start[c];
-    const int n = (int)(local / (uint32_t)f.Hc[c]);
-    const int h = f.heads[c][local - (uint32_t)n * (uint32_t)f.Hc[c]];
-    switch (f.bits[c]) {
+    const int n = (int)(b / (uint32_t)f.a.H);
+    const int h = (int)(b - (uint32_t)n * (uint32_t)f.a.H);
+    switch (f.head_bits[h]) {
     case 32: tile128<32, T, UPDATE>(f.a, n, h, sm); break;
     case 16: tile128<16, T, UPDATE>(f.a, n, h, sm); break;
     case 8: tile128<8, T, UPDATE>(f.a, n, h, sm); break;

@@ -27,16 +27,11 @@ struct StepArgs {
 
 enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2 };
 
-// One launch over every width class of a d_k = d_v = 128 pool: block b
-// belongs to class c with start[c] <= b < start[c+1]; inside a class the
-// block is request (b - start[c]) / Hc[c], head heads[c][(b - start[c]) % Hc[c]].
+// One launch over every tile of a d_k = d_v = 128 pool: block b is request
+// b / H, head b % H, whose width is head_bits[h].
 struct FusedArgs {
     StepArgs a;
-    const int32_t *heads[5];
-    int32_t Hc[5];
-    int32_t bits[5];
-    uint32_t start[5];
-    int32_t n_classes;
+    const uint8_t *head_bits;  // [H], device
 };
 
 // Enqueue `op` for the n_req x Hc tiles of one width class.  bits in
