@@ -159,7 +159,17 @@ def outlier_gains(w: Workload):
     return gr, gc
 
 
+_GAIN_CACHE: dict = {}
+
+
 def _gain_vectors(w: Workload, device="cpu"):
+    key = (w.name, w.seed, w.n_heads, w.dk, w.dv, w.tiny_recipe, str(device))
+    if key not in _GAIN_CACHE:
+        _GAIN_CACHE[key] = _make_gain_vectors(w, device)
+    return _GAIN_CACHE[key]
+
+
+def _make_gain_vectors(w: Workload, device):
     rows, cols = outlier_positions(w)
     gr, gc = outlier_gains(w)
     rg = torch.ones(w.n_heads, w.dk, dtype=torch.float32)
