@@ -145,7 +145,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first; launch times settle after ~10-15 launches")
     ap.add_argument("--workload", default="serving", choices=["serving", "highconc", "layer", "drift"])
     ap.add_argument("--distinct-inputs", type=int, default=16,
                     help="distinct pre-generated step inputs, cycled over the timed steps")

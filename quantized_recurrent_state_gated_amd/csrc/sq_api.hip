@@ -197,11 +197,19 @@ static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16,
     if (op != sqk::OP_STORE && p->dk == 128 && p->dv == 128) {
         const uint64_t total = (uint64_t)n_req * (uint64_t)p->n_heads;
         if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
-        sqk::FusedArgs f;
-        f.a = a;
-        f.head_bits = p->d_bits;
-        if (sqk::launch_fused128(op, bf16, f, (uint32_t)total, (hipStream_t)stream) != hipSuccess)
-            return SQ_ERR_HIP;
+        if (p->n_class[4] < p->n_heads) {  // any 4/6/8/16-bit heads
+            sqk::FusedArgs f;
+            f.a = a;
+            f.head_bits = p->d_bits;
+            if (sqk::launch_fused128(op, bf16, f, (uint32_t)total, (hipStream_t)stream) != hipSuccess)
+                return SQ_ERR_HIP;
+        }
+        if (p->n_class[4] > 0) {  // FP32 heads
+            a.heads = p->d_heads[4];
+            a.Hc = p->n_class[4];
+            if (sqk::launch_f32_128(op, bf16, a, n_req, (hipStream_t)stream) != hipSuccess)
+                return SQ_ERR_HIP;
+        }
         return SQ_OK;
     }
     for (int oc = 0; oc < 5; oc++) {

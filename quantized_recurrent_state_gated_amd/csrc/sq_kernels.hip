@@ -269,13 +269,14 @@ __device__ __forceinline__ float wave_sum(float x)
 
 struct Smem128 {
     float w[128], g[128], a[128];  // per-row factors k_i r_i, q_i r_i, beta k_i / r_i
+    alignas(16) float4 wg[128];    // per-row {w 2^-s0, w 2^-s1, g 2^-s0, g 2^-s1} (half codes)
     alignas(16) float red[8][2][128];  // [row group][u, y][column] partial sums
     alignas(16) float b[128];      // per-column (v_j - alpha u_j) / c_j
     float sum[2][3];               // per-wave partials of q.k, sum w, sum g
 };
 
 template <int BITS, typename T, bool UPDATE>
-__device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128 &sm)
+__device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, Smem128 &sm)
 {
     constexpr int W = BITS / 2;
     constexpr bool QUANT = BITS <= 8;
@@ -388,23 +389,257 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
     }
 }
 
-template <typename T, bool UPDATE>
-__global__ __launch_bounds__(256) void k_step128(FusedArgs f)
+// ---------------------------------------------------------------- packed-half codes
+//
+// For 4/6/8-bit codes and FP16 pivots a thread keeps its 64 elements as 32
+// dwords of packed 16-bit halves.  A code n is placed in the low mantissa
+// bits of a half whose exponent field is zero, so the half is exactly the
+// binary16 subnormal n * 2^s (s = -24, or -22 / -20 where the field sits 2 /
+// 4 bits up in its half); v_fma_mix_f32 takes it as an exact fp32 operand.
+// The power of two 2^-s is folded into the per-row weights (pass 1) and into
+// the gate (pass 2), so the codes need only masks, shifts and byte permutes.
+// FP16 pivot halves are their own values (s = 0).
+//
+// HalfPos<BITS>: element e = 4*col + row of a block sits in half sel(e) of
+// packed dword k(e), with scale class cls(e) (2^s0 or 2^s1).
+
+template <int BITS>
+struct HalfPos;
+template <>
+struct HalfPos<8> {  // dword 2c + (r & 1) = rows {0,2} or {1,3} of column c
+    static constexpr int k(int e) { return 2 * (e >> 2) + (e & 1); }
+    static constexpr int sel(int e) { return (e >> 1) & 1; }
+    static constexpr int cls(int) { return 0; }
+    static constexpr int s0 = -24, s1 = -24;
+};
+template <>
+struct HalfPos<4> {  // dword 4(c/2) + r = row r of columns c, c+1; odd rows 4 bits up
+    static constexpr int k(int e) { return 4 * (e >> 3) + (e & 3); }
+    static constexpr int sel(int e) { return (e >> 2) & 1; }
+    static constexpr int cls(int e) { return e & 1; }
+    static constexpr int s0 = -24, s1 = -20;
+};
+template <>
+struct HalfPos<6> {  // field pairs (0,3) (1,4) (2,5) (6,9) (7,10) (8,11) (12,15) (13,14)
+    static constexpr int kk[16] = {0, 1, 2, 0, 1, 2, 3, 4, 5, 3, 4, 5, 6, 7, 7, 6};
+    static constexpr int ss[16] = {0, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 0, 0, 1, 1};
+    static constexpr int k(int e) { return kk[e]; }
+    static constexpr int sel(int e) { return ss[e]; }
+    static constexpr int cls(int e) { return (ss[e] && e != 14) ? 1 : 0; }
+    static constexpr int s0 = -24, s1 = -22;
+};
+template <>
+struct HalfPos<16> {
+    static constexpr int k(int e) { return e >> 1; }
+    static constexpr int sel(int e) { return e & 1; }
+    static constexpr int cls(int) { return 0; }
+    static constexpr int s0 = 0, s1 = 0;
+};
+
+template <int BITS>
+__device__ __forceinline__ void to_halves(const uint32_t (&d)[BITS / 2], uint32_t (&hv)[8])
+{
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            hv[2 * c] = __builtin_amdgcn_perm(d[c], d[c], 0x0c020c00u);      // bytes 0, 2
+            hv[2 * c + 1] = __builtin_amdgcn_perm(d[c], d[c], 0x0c030c01u);  // bytes 1, 3
+        }
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            const uint32_t p = __builtin_amdgcn_perm(d[w], d[w], 0x0c030c01u);
+            hv[4 * w] = d[w] & 0x000f000fu;
+            hv[4 * w + 1] = d[w] & 0x00f000f0u;
+            hv[4 * w + 2] = p & 0x000f000fu;
+            hv[4 * w + 3] = p & 0x00f000f0u;
+        }
+    } else if constexpr (BITS == 6) {
+        constexpr uint32_t M = 0x00fc003fu;  // a field at bits 0-5 and one at 18-23
+        hv[0] = d[0] & M;
+        hv[1] = (d[0] >> 6) & M;
+        hv[2] = __builtin_amdgcn_alignbit(d[1], d[0], 12) & M;
+        hv[3] = (d[1] >> 4) & M;
+        hv[4] = __builtin_amdgcn_alignbit(d[2], d[1], 10) & M;
+        hv[5] = __builtin_amdgcn_alignbit(d[2], d[1], 16) & M;
+        hv[6] = (d[2] >> 8) & M;
+        hv[7] = __builtin_amdgcn_ubfe(d[2], 14, 6) | ((d[2] >> 4) & 0x003f0000u);
+    } else {
+#pragma unroll
+        for (int w = 0; w < 8; w++) hv[w] = d[w];
+    }
+#pragma unroll
+    for (int w = 0; w < 8; w++) asm volatile("" : "+v"(hv[w]));  // keep the halves opaque
+}
+
+__device__ __forceinline__ float half_of(uint32_t x, int sel)
+{
+    const __half2 hh = __builtin_bit_cast(__half2, x);
+    return sel ? __high2float(hh) : __low2float(hh);
+}
+
+template <int BITS, typename T, bool UPDATE, int TPB>
+__device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128 &sm)
+{
+    // TPB threads per tile: RG = TPB / 32 row groups, MB = 32 / RG blocks per thread
+    constexpr int RG = TPB / 32, MB = 32 / RG;
+    using P = HalfPos<BITS>;
+    constexpr int W = BITS / 2;
+    constexpr bool QUANT = BITS <= 8;
+    constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
+    constexpr int BLK_BYTES = 2 * BITS;
+    constexpr bool NT = QUANT;  // code tiles stream nontemporally (measured faster)
+    constexpr float SC0 = P::s0 == 0 ? 1.0f : (P::s0 == -24 ? 16777216.0f : 0.0f);
+    constexpr float SC1 = P::s1 == 0 ? 1.0f : (P::s1 == -24 ? 16777216.0f : (P::s1 == -22 ? 4194304.0f : 1048576.0f));
+    static_assert(SC0 > 0.0f, "scale");
+
+    const int t = threadIdx.x;
+    const int cb = t & 31, rg = t >> 5;
+    const long nh = (long)n * a.H + h;
+    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const T *q = reinterpret_cast<const T *>(a.q);
+    const T *k = reinterpret_cast<const T *>(a.k);
+    const T *v = reinterpret_cast<const T *>(a.v);
+
+    // block (rg + RG m, cb) of the tile; the 64 lanes of a wave cover 64
+    // consecutive blocks for every m (global loads measured faster on gfx950
+    // than buffer loads with a per-tile resource)
+    uint32_t hv[MB][8];
+    {
+        uint32_t d[MB][W];
+#pragma unroll
+        for (int m = 0; m < MB; m++)
+            load_block<BITS, NT>(tile + (long)((rg + RG * m) * 32 + cb) * BLK_BYTES, d[m]);
+#pragma unroll
+        for (int m = 0; m < MB; m++) to_halves<BITS>(d[m], hv[m]);
+    }
+
+    const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
+    const float beta = UPDATE ? a.beta[nh] : 0.0f;
+
+    if (t < 128) {
+        const float qi = ld1(q, nh * 128 + t);
+        const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
+        const float ri = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
+        const float wi = ki * ri, gi = qi * ri;
+        sm.wg[t] = make_float4(wi * SC0, wi * SC1, gi * SC0, gi * SC1);
+        if (UPDATE) sm.a[t] = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
+        if ((t & 63) == 0) {
+            sm.sum[t >> 6][0] = s0;
+            sm.sum[t >> 6][1] = s1;
+            sm.sum[t >> 6][2] = s2;
+        }
+    }
+    __syncthreads();
+
+    // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
+    float pu[4] = {0, 0, 0, 0}, py[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < MB; m++) {
+        const int i0 = 4 * (rg + RG * m);
+#pragma unroll
+        for (int ri = 0; ri < 4; ri++) {
+            const float4 f = sm.wg[i0 + ri];
+#pragma unroll
+            for (int cj = 0; cj < 4; cj++) {
+                const int e = 4 * cj + ri;
+                const float x = half_of(hv[m][P::k(e)], P::sel(e));
+                const float w = P::cls(e) ? f.y : f.x;
+                const float g = P::cls(e) ? f.w : f.z;
+                if (UPDATE) pu[cj] = fmaf(w, x, pu[cj]);
+                py[cj] = fmaf(g, x, py[cj]);
+            }
+        }
+    }
+    *reinterpret_cast<float4 *>(&sm.red[rg][0][4 * cb]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
+    *reinterpret_cast<float4 *>(&sm.red[rg][1][4 * cb]) = make_float4(py[0], py[1], py[2], py[3]);
+    __syncthreads();
+
+    // column finalisation: thread j < 128 owns column j
+    if (t < 128) {
+        float U = 0.0f, Y = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RG; r++) {
+            U += sm.red[r][0][t];
+            Y += sm.red[r][1][t];
+        }
+        const float qk = sm.sum[0][0] + sm.sum[1][0];
+        const float Wsum = sm.sum[0][1] + sm.sum[1][1];
+        const float Gsum = sm.sum[0][2] + sm.sum[1][2];
+        const float cjs = QUANT ? a.csc[(long)h * 128 + t] : 1.0f;
+        const float uj = cjs * (U - OFF * Wsum);
+        const float yj = cjs * (Y - OFF * Gsum);
+        if (!UPDATE) {
+            a.o[nh * 128 + t] = yj;
+        } else {
+            const float e = ld1(v, nh * 128 + t) - alpha * uj;
+            if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * qk * e);
+            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cjs) : e;
+        }
+    }
+    if (!UPDATE) return;
+    __syncthreads();
+    const float4 b4 = *reinterpret_cast<const float4 *>(&sm.b[4 * cb]);
+    const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+    // the halves are read again in pass 2: keeping them opaque makes the
+    // compiler fold the conversion into v_fma_mix_f32 there too instead of
+    // keeping 64 converted floats alive across the reduction
+#pragma unroll
+    for (int m = 0; m < MB; m++)
+#pragma unroll
+        for (int w = 0; w < 8; w++) asm volatile("" : "+v"(hv[m][w]));
+
+    // pass 2: z = alpha n + a_i b_j + OFF (1 - alpha), requantize, repack, store
+    const float C = OFF * (1.0f - alpha);
+    const float al0 = alpha * SC0, al1 = alpha * SC1;  // alpha n = (alpha 2^-s) (n 2^s)
+#pragma unroll
+    for (int m = 0; m < MB; m++) {
+        const int i0 = 4 * (rg + RG * m);
+        float z[16];
+#pragma unroll
+        for (int ri = 0; ri < 4; ri++) {
+            const float ai = sm.a[i0 + ri];
+#pragma unroll
+            for (int cj = 0; cj < 4; cj++) {
+                const int e = 4 * cj + ri;
+                const float x = half_of(hv[m][P::k(e)], P::sel(e));
+                z[e] = fmaf(P::cls(e) ? al1 : al0, x, fmaf(ai, b[cj], C));
+            }
+        }
+        uint32_t dn[W];
+        encode<BITS>(z, dn);
+        store_block<BITS, NT>(tile + (long)((rg + RG * m) * 32 + cb) * BLK_BYTES, dn);
+    }
+}
+
+template <typename T, bool UPDATE, int TPB, int WPE>
+__global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void k_step128(FusedArgs f)
 {
     // block b is request b / H, head b % H: the grid walks the pool in memory
     // order, so tiles of every width are interleaved on each CU (VALU-heavy
-    // narrow codes overlap with memory-heavy wide tiles)
+    // narrow codes overlap with memory-heavy wide tiles).  FP32 heads are
+    // skipped here and run in k_step128_f32.
     __shared__ Smem128 sm;
     const uint32_t b = blockIdx.x;
     const int n = (int)(b / (uint32_t)f.a.H);
     const int h = (int)(b - (uint32_t)n * (uint32_t)f.a.H);
     switch (f.head_bits[h]) {
-    case 32: tile128<32, T, UPDATE>(f.a, n, h, sm); break;
-    case 16: tile128<16, T, UPDATE>(f.a, n, h, sm); break;
-    case 8: tile128<8, T, UPDATE>(f.a, n, h, sm); break;
-    case 6: tile128<6, T, UPDATE>(f.a, n, h, sm); break;
-    default: tile128<4, T, UPDATE>(f.a, n, h, sm); break;
+    case 16: tile128<16, T, UPDATE, TPB>(f.a, n, h, sm); break;
+    case 8: tile128<8, T, UPDATE, TPB>(f.a, n, h, sm); break;
+    case 6: tile128<6, T, UPDATE, TPB>(f.a, n, h, sm); break;
+    case 4: tile128<4, T, UPDATE, TPB>(f.a, n, h, sm); break;
+    default: break;
     }
+}
+
+template <typename T, bool UPDATE>
+__global__ __launch_bounds__(256) void k_step128_f32(StepArgs a)
+{
+    __shared__ Smem128 sm;
+    const int n = blockIdx.x / a.Hc;
+    const int h = a.heads[blockIdx.x - n * a.Hc];
+    tile128_wide<32, T, UPDATE>(a, n, h, sm);
 }
 
 // ---------------------------------------------------------------- any shape
@@ -589,22 +824,48 @@ static hipError_t launch_t(Op op, int bits, const StepArgs &a, int32_t n_req, hi
     }
 }
 
+hipError_t launch_f32_128(Op op, bool qkv_bf16, const StepArgs &a, int32_t n_req, hipStream_t st)
+{
+    if (n_req <= 0 || a.Hc <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((long)n_req * a.Hc));
+    if (op == OP_STEP) {
+        if (qkv_bf16)
+            hipLaunchKernelGGL((k_step128_f32<uint16_t, true>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_step128_f32<float, true>), grid, dim3(256), 0, st, a);
+    } else {
+        if (qkv_bf16)
+            hipLaunchKernelGGL((k_step128_f32<uint16_t, false>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_step128_f32<float, false>), grid, dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <int TPB, int WPE>
+static void fused128(Op op, bool qkv_bf16, const FusedArgs &f, dim3 grid, hipStream_t st)
+{
+    if (op == OP_STEP) {
+        if (qkv_bf16)
+            hipLaunchKernelGGL((k_step128<uint16_t, true, TPB, WPE>), grid, dim3(TPB), 0, st, f);
+        else
+            hipLaunchKernelGGL((k_step128<float, true, TPB, WPE>), grid, dim3(TPB), 0, st, f);
+    } else {
+        if (qkv_bf16)
+            hipLaunchKernelGGL((k_step128<uint16_t, false, TPB, WPE>), grid, dim3(TPB), 0, st, f);
+        else
+            hipLaunchKernelGGL((k_step128<float, false, TPB, WPE>), grid, dim3(TPB), 0, st, f);
+    }
+}
+
 hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,
                           hipStream_t st)
 {
     if (n_blocks == 0) return hipSuccess;
     const dim3 grid(n_blocks);
-    if (op == OP_STEP) {
-        if (qkv_bf16)
-            hipLaunchKernelGGL((k_step128<uint16_t, true>), grid, dim3(256), 0, st, f);
-        else
-            hipLaunchKernelGGL((k_step128<float, true>), grid, dim3(256), 0, st, f);
-    } else {
-        if (qkv_bf16)
-            hipLaunchKernelGGL((k_step128<uint16_t, false>), grid, dim3(256), 0, st, f);
-        else
-            hipLaunchKernelGGL((k_step128<float, false>), grid, dim3(256), 0, st, f);
-    }
+    // two waves per tile, each thread holding eight 4x4 blocks as packed
+    // halves; the register budget is held to 5 waves per SIMD
+    fused128<128, 5>(op, qkv_bf16, f, grid, st);
     return hipGetLastError();
 }
 

@@ -40,7 +40,11 @@ struct FusedArgs {
 hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
                   hipStream_t stream);
 
-// Step or readout over all classes of a d = 128 pool in one launch.
+// Step or readout over the FP32 heads (a.heads / a.Hc) of a d = 128 pool.
+hipError_t launch_f32_128(Op op, bool qkv_bf16, const StepArgs &a, int32_t n_req,
+                          hipStream_t stream);
+
+// Step or readout over the 4/6/8/16-bit tiles of a d = 128 pool in one launch.
 hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,
                           hipStream_t stream);
 
