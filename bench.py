@@ -111,6 +111,46 @@ def trace_summary(stats_csv: str) -> int:
     return 0
 
 
+def fp32_state_baseline(sq, I, w, dev, stream, ins, quant_ms, steps=16, warmup=10):
+    """The same step with every head holding an unquantized FP32 state (the
+    'FP32 state' baseline of the pages' efficiency comparison), timed on the
+    same inputs; context for the quantized step, not part of the metric."""
+    import numpy as np
+    import torch
+
+    bits = np.full(w.n_heads, 32, np.uint8)
+    nbytes = sq.sq_pool_bytes(w.n_req, w.n_heads, w.dk, w.dv, bits)
+    ones_r = torch.ones(w.n_heads, w.dk, device=dev)
+    ones_c = torch.ones(w.n_heads, w.dv, device=dev)
+    state = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pool = sq.sq_pool_alloc(w.n_req, w.n_heads, w.dk, w.dv, bits, ones_r, ones_c, state)
+    slots = torch.arange(w.n_req, dtype=torch.int32, device=dev)
+    for p in range(w.n_req):
+        sq.sq_pool_store(pool, slots[p:p + 1], I.initial_state(w, p, dev))
+    o = torch.empty(w.n_req, w.n_heads, w.dv, device=dev)
+
+    def step(t):
+        x = ins[t % len(ins)]
+        sq.sq_decode_step(pool, slots, x.q, x.k, x.v, x.alpha, x.beta, o, stream)
+
+    for t in range(warmup):
+        step(t)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for t in range(steps):
+        step(warmup + t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    byts = algorithmic_bytes_per_step(w, bits)
+    del pool, state
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "hbm_gbps": byts / (ms / 1e3) / 1e9, "pool_bytes": nbytes,
+            "speedup_of_quantized_step": ms / quant_ms,
+            "pages_context": "2.91x state-update speedup at 6 bits on NVIDIA A800"}
+
+
 def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
     """The oracle, as it stands, on a bounded sample: whole requests (all 2304
     heads) of the same workload, calibrated to about target_s seconds."""
@@ -153,6 +193,8 @@ def main() -> int:
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp32-baseline", action="store_true",
+                    help="skip timing the unquantized FP32-state step at the same shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -285,6 +327,11 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+
+    if not args.no_fp32_baseline:
+        result["fp32_state_baseline"] = fp32_state_baseline(sq, I, w, dev, stream, ins, ms_per_step)
+        log(f"[bench] FP32-state step: {result['fp32_state_baseline']['ms_per_step']:.3f} ms "
+            f"({result['fp32_state_baseline']['speedup_of_quantized_step']:.2f}x)")
 
     if not args.no_cpu_baseline:
         del ins

@@ -192,7 +192,7 @@ def initial_state(w: Workload, req: int, device="cpu") -> torch.Tensor:
     return G * STATE_SIGMA * rg[:, :, None] * cg[:, None, :]
 
 
-def scales(w: Workload, device="cpu", chunk: int = 8):
+def scales(w: Workload, device="cpu", chunk: int = 8, bits=None):
     """Per-head row and column factors r[H][dk], c[H][dv] (fp32).
 
     tiny: r_i = 1 and c_j ~ LogUniform(0.5, 2) read as the column's range, so
@@ -200,8 +200,9 @@ def scales(w: Workload, device="cpu", chunk: int = 8):
     request's S0 (a stand-in for the pages' offline fitting, [P5] 空间维度):
     r_i = max |S0_ij| over requests and columns, then
     c_j = max over requests and rows of |S0_ij| / r_i, divided by Q_b, so that
-    no element of S0 exceeds the code range.  Pivot and FP32 heads get 1."""
-    bits = head_bits(w)
+    no element of S0 exceeds the code range.  Pivot and FP32 heads get 1.
+    `bits` overrides the workload's width table (e.g. a uniform comparator)."""
+    bits = head_bits(w) if bits is None else np.asarray(bits, np.uint8)
     Qb = torch.tensor([(2 ** (int(b) - 1) - 1) if b <= 8 else 1 for b in bits], dtype=torch.float32)
     if w.tiny_recipe:
         rng = _rng(w, 3)

@@ -85,3 +85,13 @@ def test_tiny_recipe():
     si = I.step_inputs(w, 0)
     assert si.q.dtype == torch.float32
     assert float((si.k.norm(dim=-1) - 1).abs().max()) < 1e-6
+
+
+def test_spearman_helper_matches_scipy():
+    from scipy.stats import spearmanr
+    from quantized_recurrent_state_gated_amd.drift import spearman
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal(200)
+    b = a + rng.standard_normal(200)
+    b[:20] = b[0]  # ties
+    assert abs(spearman(a, b) - spearmanr(a, b).correlation) < 1e-12
