@@ -126,6 +126,16 @@ int sq_pool_tile_offset(const sq_pool *pool, int32_t slot, int32_t head, uint64_
 int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const float *S,
                   void *stream);
 
+/* Load-and-dequantize, the inverse of sq_pool_store: write the states of slots
+ * slot_ids[0..n_req) (DEVICE int32) as fp32 S[n_req][n_heads][d_k][d_v]
+ * (DEVICE, row-major, 16-byte aligned).  Each element is the stored value
+ * rounded once to fp32: fl32(q * fl32(r_i c_j)) for codes, the binary16 value
+ * for pivots, the stored value for FP32 heads.  The pool is not modified.
+ * n_req == 0 is a no-op.  Asynchronous on `stream`.  (Calibration,
+ * checkpoint export, inspection.) */
+int sq_pool_load(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, float *S,
+                 void *stream);
+
 /* One fused decode step for a batch of n_req requests (see the top of this
  * file).  All pointers DEVICE, row-major:
  *   slot_ids int32 [n_req], each in [0, n_slots), no duplicates;

@@ -71,6 +71,8 @@ def _load():
                                     _f32p, _i32p, ctypes.c_int, _f32p, _f32p, ctypes.c_int]),
         "orc_store_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
                                   _f32p, _i32p, ctypes.c_int, _f32p]),
+        "orc_load_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
+                                 _f32p, _i32p, ctypes.c_int, _f32p]),
         "orc_bruteforce": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p, _f64p,
                                   _f64p, _f64p, _f64p, _f64p, _f64p]),
     }
@@ -244,6 +246,18 @@ def store_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, S)
     assert S.size == sid.size * hb.size * dk * dv
     _load().orc_store_pool(_p(pool, _u8p), hb.size, dk, dv, _p(hb, _u8p), _p(r, _f32p),
                            _p(c, _f32p), _p(sid, _i32p), sid.size, _p(S, _f32p))
+
+
+def load_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids) -> np.ndarray:
+    """Decoded fp32 states S[n_req][H][dk][dv] of the slots' tiles."""
+    pool = _c(pool, np.uint8)
+    hb = _c(head_bits, np.uint8)
+    sid = _c(slot_ids, np.int32)
+    r, c = _c(r, np.float32), _c(c, np.float32)
+    S = np.empty((sid.size, hb.size, dk, dv), np.float32)
+    _load().orc_load_pool(_p(pool, _u8p), hb.size, dk, dv, _p(hb, _u8p), _p(r, _f32p),
+                          _p(c, _f32p), _p(sid, _i32p), sid.size, _p(S, _f32p))
+    return S
 
 
 def bruteforce(S0, q, k, v, alpha, beta):

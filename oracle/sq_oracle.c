@@ -521,3 +521,24 @@ void orc_f16_to_f32_array(const uint16_t *h, float *x, long n)
 {
     for (long e = 0; e < n; e++) x[e] = orc_f16_to_f32(h[e]);
 }
+
+/* Load-and-dequantize: write the states of slots slot_ids[n] as fp32
+ * S[n_req][H][d_k][d_v] (row-major), each element the decoded value rounded
+ * once to fp32 (codes: fl32(q * s_ij); pivots: the binary16 value; FP32: the
+ * stored value). */
+void orc_load_pool(const uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
+                   const float *r, const float *c, const int32_t *slot_ids, int n_req, float *S)
+{
+    int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
+    long slab = orc_pool_layout(n_heads, head_bits, dk, dv, off);
+    double *D = (double *)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+    for (int n = 0; n < n_req; n++)
+        for (int h = 0; h < n_heads; h++) {
+            orc_decode_tile(head_bits[h], dk, dv, pool + (long)slot_ids[n] * slab + off[h],
+                            r + (long)h * dk, c + (long)h * dv, D);
+            float *dst = S + ((long)n * n_heads + h) * (long)dk * dv;
+            for (long e = 0; e < (long)dk * dv; e++) dst[e] = (float)D[e];
+        }
+    free(D);
+    free(off);
+}

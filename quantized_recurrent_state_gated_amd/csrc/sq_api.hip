@@ -194,7 +194,7 @@ static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16,
     // d = 128: one launch over all tiles in pool order; otherwise one launch
     // per width class, widest tiles first
     static const int order[5] = {4, 3, 2, 1, 0};
-    if (op != sqk::OP_STORE && p->dk == 128 && p->dv == 128) {
+    if ((op == sqk::OP_STEP || op == sqk::OP_READOUT) && p->dk == 128 && p->dv == 128) {
         const uint64_t total = (uint64_t)n_req * (uint64_t)p->n_heads;
         if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
         if (p->n_class[4] < p->n_heads) {  // any 4/6/8/16-bit heads
@@ -232,6 +232,17 @@ int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const f
     sqk::StepArgs a = base_args(pool, slot_ids);
     a.S = S;
     return run_classes(pool, sqk::OP_STORE, a, false, n_req, stream);
+}
+
+int sq_pool_load(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, float *S,
+                 void *stream)
+{
+    if (!pool || n_req < 0) return SQ_ERR_INVALID;
+    if (n_req == 0) return SQ_OK;
+    if (n_req > pool->n_slots || !slot_ids || !S || !aligned(S, 16)) return SQ_ERR_INVALID;
+    sqk::StepArgs a = base_args(pool, slot_ids);
+    a.S = S;
+    return run_classes(pool, sqk::OP_LOAD, a, false, n_req, stream);
 }
 
 int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,

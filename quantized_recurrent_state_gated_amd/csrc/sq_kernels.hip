@@ -792,15 +792,62 @@ __global__ __launch_bounds__(256) void k_store(StepArgs a, long total_blocks)
     for (int w = 0; w < W; w++) dst[w] = dd[w];
 }
 
+// ---------------------------------------------------------------- load
+//
+// Dequantize tiles into fp32 row-major states: one thread per 4x4 block;
+// element value = fl32(q * fl32(r_i c_j)) for codes, the binary16 value for
+// pivots, the stored value for FP32 heads.
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_load(StepArgs a, float *S, long total_blocks)
+{
+    constexpr int W = BITS / 2;
+    constexpr bool QUANT = BITS <= 8;
+    constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= total_blocks) return;
+    const int dk = a.dk, dv = a.dv;
+    const long nblk = (long)(dk >> 2) * (dv >> 2);
+    const long tix = gid / nblk;
+    const long B = gid - tix * nblk;
+    const int n = (int)(tix / a.Hc);
+    const int h = a.heads[tix - (long)n * a.Hc];
+    const long nh = (long)n * a.H + h;
+    const uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const int i0 = 4 * (int)(B / (dv >> 2)), j0 = 4 * (int)(B % (dv >> 2));
+    uint32_t dd[W];
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + B * 2 * BITS);
+#pragma unroll
+    for (int w = 0; w < W; w++) dd[w] = src[w];
+    float f[16];
+    decode<BITS>(dd, f);
+    float *dst = S + nh * (long)dk * dv;
+#pragma unroll
+    for (int cj = 0; cj < 4; cj++)
+#pragma unroll
+        for (int ri = 0; ri < 4; ri++) {
+            float x = f[4 * cj + ri];
+            if constexpr (QUANT) {
+                const float s = a.rsc[(long)h * dk + i0 + ri] * a.csc[(long)h * dv + j0 + cj];
+                x = (x - OFF) * s;  // the code is exact; one rounding of q * s
+            }
+            dst[(long)(i0 + ri) * dv + j0 + cj] = x;
+        }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 template <int BITS, typename T>
 static hipError_t launch_bits(Op op, const StepArgs &a, int32_t n_req, hipStream_t st)
 {
-    if (op == OP_STORE) {
+    if (op == OP_STORE || op == OP_LOAD) {
         const long total = (long)n_req * a.Hc * (a.dk / 4) * (a.dv / 4);
         const long grid = (total + 255) / 256;
-        hipLaunchKernelGGL((k_store<BITS>), dim3((unsigned)grid), dim3(256), 0, st, a, total);
+        if (op == OP_STORE)
+            hipLaunchKernelGGL((k_store<BITS>), dim3((unsigned)grid), dim3(256), 0, st, a, total);
+        else
+            hipLaunchKernelGGL((k_load<BITS>), dim3((unsigned)grid), dim3(256), 0, st, a,
+                               const_cast<float *>(a.S), total);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((long)n_req * a.Hc));

@@ -22,10 +22,10 @@ struct StepArgs {
     const void *q, *k, *v;     // [n_req][H][d]
     const float *alpha, *beta; // [n_req][H]
     float *o;                  // [n_req][H][dv] or null
-    const float *S;            // store only: [n_req][H][dk][dv]
+    const float *S;            // store: source, load: destination, [n_req][H][dk][dv]
 };
 
-enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2 };
+enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2, OP_LOAD = 3 };
 
 // One launch over every tile of a d_k = d_v = 128 pool: block b is request
 // b / H, head b % H, whose width is head_bits[h].

@@ -54,11 +54,14 @@ def spearman(a, b) -> float:
 
 
 class Run:
-    def __init__(self, w, bits, dev):
+    def __init__(self, w, bits, dev, scales=None):
         from . import sq  # the HIP library; raises if it is not built
         self.sq = sq
         self.bits = np.asarray(bits, np.uint8)
-        self.r, self.c = I.scales(w, device=dev, bits=self.bits)
+        if scales is None:
+            self.r, self.c = I.scales(w, device=dev, bits=self.bits)
+        else:
+            self.r, self.c = (x.to(dev).float().contiguous() for x in scales)
         nbytes = self.sq.sq_pool_bytes(w.n_req, w.n_heads, w.dk, w.dv, self.bits)
         self.state = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.pool = self.sq.sq_pool_alloc(w.n_req, w.n_heads, w.dk, w.dv, self.bits, self.r, self.c,
@@ -73,7 +76,8 @@ class Run:
         return self.o
 
 
-def report(workload: str = "drift", steps: int | None = None, device: str = "cuda") -> dict:
+def report(workload: str = "drift", steps: int | None = None, device: str = "cuda",
+           calibrated: bool = False) -> dict:
     w = I.WORKLOADS[workload]
     steps = steps or w.steps
     dev = torch.device(device)
@@ -82,6 +86,33 @@ def report(workload: str = "drift", steps: int | None = None, device: str = "cud
                "uniform_int8": np.full(H, 8, np.uint8)}
     ref = Run(w, np.full(H, 32, np.uint8), dev)
     runs = {k: Run(w, b, dev) for k, b in formats.items()}
+    calib_info = {}
+    if calibrated:
+        from . import calibrate as CAL
+        bits0 = formats["mixed"]
+        n_piv = int((bits0 == 16).sum())
+        mean_bits = float(np.mean(bits0[bits0 <= 8]))
+        t0 = time.time()
+        cal = CAL.calibrate(w, mean_bits, n_piv, device=device)
+        print(f"[drift] calibration: {cal['report']} ({time.time() - t0:.1f} s)", flush=True)
+        # spatial part alone: the half-life-ranked widths with fitted factors
+        S = CAL.calibration_states(I.Workload(w.name + "-calib", 4, H, w.dk, w.dv, 256, dict(w.counts),
+                                              w.half_life, w.beta_range, w.qkv_dtype, w.tiny_recipe,
+                                              w.persistent_outliers, w.seed,
+                                              dict(w.extra, input_seed=w.seed + 7777)),
+                                   256, 32, 4, device)
+        wc = I.Workload(w.name + "-calib", 4, H, w.dk, w.dv, 256, dict(w.counts), w.half_life,
+                        w.beta_range, w.qkv_dtype, w.tiny_recipe, w.persistent_outliers, w.seed,
+                        dict(w.extra, input_seed=w.seed + 7777))
+        infl = CAL.row_influence(wc, 256, device)
+        r_s, c_s, hist = CAL.fit_scales(S, infl, bits0, iters=3)
+        del S
+        runs["mixed_fitted_scales"] = Run(w, bits0, dev, (r_s, c_s))
+        formats["mixed_fitted_scales"] = bits0
+        runs["calibrated"] = Run(w, cal["bits"], dev, (cal["r"], cal["c"]))
+        formats["calibrated"] = cal["bits"]
+        calib_info = {"calibrated": cal["report"],
+                      "fit_gain_mixed_widths": float((hist[-1].sum() / hist[0].sum()).item())}
     curves = {k: {"mean": [], "p50": [], "p99": []} for k in runs}
     head_sum = {k: torch.zeros(H, device=dev, dtype=torch.float64) for k in runs}
     qs = torch.tensor([0.5, 0.99], device=dev)
@@ -112,12 +143,13 @@ def report(workload: str = "drift", steps: int | None = None, device: str = "cud
         "curves": curves,
         "summary": {},
         "spearman_head_error_vs_half_life": {},
+        "calibration": calib_info,
     }
     for k in runs:
         out["summary"][k] = {str(t): {s: curves[k][s][t] for s in ("mean", "p50", "p99")}
                              for t in sorted({0, 15, 127, 511, 1023, steps - 1}) if t < steps}
         per_head = (head_sum[k] / (steps * w.n_req)).cpu().numpy()
-        quant = mixed_bits <= 8 if k == "mixed" else np.ones(H, bool)
+        quant = formats[k] <= 8
         out["spearman_head_error_vs_half_life"][k] = spearman(per_head[quant], hl[quant])
     return out
 
@@ -127,8 +159,10 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="drift")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--calibrated", action="store_true",
+                    help="also run the calibrated widths and factors (offline calibration)")
     a = ap.parse_args(argv)
-    rep = report(a.workload, a.steps)
+    rep = report(a.workload, a.steps, calibrated=a.calibrated)
     text = json.dumps(rep)
     if a.out:
         with open(a.out, "w") as f:

@@ -92,8 +92,13 @@ def _rng(w: Workload, stream: int) -> np.random.Generator:
 
 
 def _torch_gen(w: Workload, stream: int, device) -> torch.Generator:
+    """Generator for decode inputs and initial states.  They use the workload's
+    input seed (extra["input_seed"], default the workload seed); per-head
+    properties (half-lives, widths, outlier positions) always use the workload
+    seed, so a calibration decode of the same heads differs only in its inputs."""
     g = torch.Generator(device=device)
-    g.manual_seed((w.seed * 1000003 + stream * 7919) % (2 ** 62))
+    seed = int(w.extra.get("input_seed", w.seed))
+    g.manual_seed((seed * 1000003 + stream * 7919) % (2 ** 62))
     return g
 
 

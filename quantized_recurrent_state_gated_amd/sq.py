@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM = 0, -1, -2, -3, -4
 SQ_F32, SQ_BF16 = 0, 1
 EXPORTED = ("sq_pool_bytes", "sq_pool_alloc", "sq_pool_free", "sq_pool_tile_offset",
-            "sq_pool_store", "sq_decode_step", "sq_readout", "sq_status_string")
+            "sq_pool_store", "sq_pool_load", "sq_decode_step", "sq_readout", "sq_status_string")
 
 
 class SqPoolDesc(ctypes.Structure):
@@ -48,6 +48,8 @@ _lib.sq_pool_tile_offset.argtypes = [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_ui
                                      ctypes.POINTER(ctypes.c_uint64)]
 _lib.sq_pool_store.restype = ctypes.c_int
 _lib.sq_pool_store.argtypes = [_vp, _vp, _i32, _vp, _vp]
+_lib.sq_pool_load.restype = ctypes.c_int
+_lib.sq_pool_load.argtypes = [_vp, _vp, _i32, _vp, _vp]
 _lib.sq_decode_step.restype = ctypes.c_int
 _lib.sq_decode_step.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
 _lib.sq_readout.restype = ctypes.c_int
@@ -154,6 +156,13 @@ def sq_pool_store(pool: SqPool, slot_ids, S, stream=None) -> None:
     n_req = 0 if slot_ids is None else int(slot_ids.numel())
     _check(_lib.sq_pool_store(pool.handle, _ptr(slot_ids), n_req, _ptr(S), _stream(stream)),
            "sq_pool_store")
+
+
+def sq_pool_load(pool: SqPool, slot_ids, S, stream=None) -> None:
+    """Dequantize the slots' states into the fp32 device tensor S [n_req][H][dk][dv]."""
+    n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    _check(_lib.sq_pool_load(pool.handle, _ptr(slot_ids), n_req, _ptr(S), _stream(stream)),
+           "sq_pool_load")
 
 
 def sq_decode_step(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=None) -> None:

@@ -1,0 +1,101 @@
+"""Pins for the offline calibration (temporal allocation, spatial fit)."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_recurrent_state_gated_amd import calibrate as C
+from quantized_recurrent_state_gated_amd import inputs as I
+
+
+def test_allocation_dp_equals_brute_force():
+    rng = np.random.default_rng(0)
+    for trial in range(40):
+        H = int(rng.integers(1, 7))
+        L = rng.uniform(0.5, 20, H)
+        D = np.sort(rng.uniform(0, 10, (H, 3)), axis=1)[:, ::-1].copy()  # more bits, less error
+        budget = int(rng.integers(4 * H, 8 * H + 1))
+        bits = C.allocate(L, D, budget)
+        best = None
+        for combo in itertools.product(range(3), repeat=H):
+            b = sum(C.WIDTHS[i] for i in combo)
+            if b > budget:
+                continue
+            val = sum(L[h] * D[h, combo[h]] for h in range(H))
+            best = val if best is None or val < best else best
+        got = sum(L[h] * D[h, C.WIDTHS.index(int(bits[h]))] for h in range(H))
+        assert abs(got - best) < 1e-9 * max(1.0, best)
+        assert int(bits.astype(int).sum()) <= budget
+
+
+def test_allocation_budget_pivots_and_lifetime_monotone():
+    H = 40
+    L = np.linspace(1, 100, H)            # head h lives longer than head h-1
+    D = np.tile([8.0, 2.0, 0.5], (H, 1))  # identical distortion
+    bits = C.allocate(L, D, budget_bits=6 * (H - 3), n_pivots=3)
+    assert (bits == 16).sum() == 3 and set(np.nonzero(bits == 16)[0]) == {H - 1, H - 2, H - 3}
+    q = bits[bits <= 8].astype(int)
+    assert q.sum() <= 6 * (H - 3)
+    assert np.all(np.diff(q) >= 0)        # longer-lived heads never get fewer bits
+    with pytest.raises(ValueError):
+        C.allocate(L, D, budget_bits=3 * H)
+
+
+def test_row_influence_closed_form():
+    w = I.Workload("infl", 3, 2, 8, 8, 4, {8: 2}, qkv_dtype="f32", seed=5)
+    infl = C.row_influence(w, 4)
+    acc = torch.zeros(2, 8, dtype=torch.float64)
+    for t in range(4):
+        si = I.step_inputs(w, t)
+        for n in range(3):
+            for h in range(2):
+                q, k = si.q[n, h].double(), si.k[n, h].double()
+                a, b = float(si.alpha[n, h]), float(si.beta[n, h])
+                wv = a * (q - b * float(q @ k) * k)  # readout weight of an error row
+                acc[h] += wv ** 2
+    assert torch.allclose(infl.double(), acc / 12, rtol=1e-5, atol=1e-9)
+
+
+def _states(seed=0, N=6, H=3, d=16):
+    g = torch.Generator().manual_seed(seed)
+    S = torch.randn(N, H, d, d, generator=g)
+    S[:, :, 3] *= 8.0       # an outlier row
+    S[:, :, :, 5] *= 15.0   # an outlier column
+    return S
+
+
+def test_fit_starts_at_maxabs_and_never_worsens():
+    S = _states()
+    bits = np.array([4, 6, 8])
+    infl = torch.rand(3, 16, generator=torch.Generator().manual_seed(1)) + 0.1
+    r0, c0 = C.maxabs_scales(S, bits)
+    r, c, hist = C.fit_scales(S, infl, bits, iters=0)
+    assert torch.equal(r, r0) and torch.equal(c, c0)
+    r, c, hist = C.fit_scales(S, infl, bits, iters=4)
+    for a, b in zip(hist, hist[1:]):
+        assert torch.all(b <= a)
+    assert torch.all(hist[-1] < hist[0])  # the fit improves on max-abs here
+    assert torch.allclose(C.weighted_error(S, infl, r, c, bits), hist[-1])
+    # max-abs never clips: every |S| / s <= Q
+    s0 = r0[:, :, None] * c0[:, None, :]
+    for h, b in enumerate(bits):
+        assert float((S[:, h].abs() / s0[h]).max()) <= (2 ** (int(b) - 1) - 1) * (1 + 1e-6)
+
+
+def test_column_update_solves_weighted_normal_equations():
+    """With codes fixed, the column step is the WLS solution: residual
+    orthogonal to the weighted regressor."""
+    S = _states(2, N=4, H=1)
+    bits = np.array([6])
+    infl = torch.rand(1, 16, generator=torch.Generator().manual_seed(3)) + 0.1
+    r, c = C.maxabs_scales(S, bits)
+    Q = 31
+    q = C._codes(S.double(), (r.double()[:, :, None] * c.double()[:, None, :])[None], Q)
+    wi = infl.double()[None, :, :, None]
+    X = r.double()[None, :, :, None] * q
+    num = (wi * X * S.double()).sum(dim=(0, 2))
+    den = (wi * X * X).sum(dim=(0, 2))
+    cj = num / den
+    resid = S.double() - cj[None, :, None, :] * X
+    assert torch.allclose((wi * X * resid).sum(dim=(0, 2)), torch.zeros_like(cj), atol=1e-9)

@@ -110,6 +110,27 @@ def test_store_bit_exact(sq, orc, name, shape):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (12, 20)])
+def test_load_bit_exact(sq, orc, dk, dv):
+    w = I.Workload("load", 2, 5, dk, dv, 2, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=dk + dv)
+    case = Case(sq, orc, w, n_slots=4, slots=[3, 1])
+    case.step(I.step_inputs(w, 0))  # load a state that has been through a step
+    host = case.host()
+    S = torch.empty(w.n_req, w.n_heads, dk, dv, device="cuda")
+    sq.sq_pool_load(case.pool, case.slots_d, S)
+    want = orc.load_pool(host, case.bits, dk, dv, case.r, case.c, case.slots)
+    got = S.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # store(load(x)) reproduces the tiles bit for bit
+    before = case.host().copy()
+    case.dev.zero_()
+    sq.sq_pool_store(case.pool, case.slots_d, S)
+    after = case.host()
+    for p in case.slots:
+        assert np.array_equal(after[p * case.slab:(p + 1) * case.slab],
+                              before[p * case.slab:(p + 1) * case.slab])
+
+
 # ------------------------------------------------------------------ step parity
 
 def test_tiny_all_steps(sq, orc):

@@ -348,3 +348,33 @@ def test_store_pool_matches_encode(orc):
     for h in range(H):
         t = orc.encode_tile(int(bits[h]), dk, dv, S[0, h].astype(np.float64), r[h], c[h])
         assert np.array_equal(pool[slab + off[h]: slab + off[h] + t.size], t)
+
+
+def test_load_after_store_is_within_half_a_step(orc):
+    """load(store(S)) differs from S by at most half a step in range (codes),
+    rounds to binary16 (pivots), and is the identity for FP32 states."""
+    rng = np.random.default_rng(92)
+    dk, dv = 16, 12
+    bits = np.array([4, 6, 8, 16, 32], np.uint8)
+    H = bits.size
+    off, slab = orc.pool_layout(bits, dk, dv)
+    pool = np.zeros(3 * slab, np.uint8)
+    r = _f32(rng.uniform(0.5, 2, (H, dk)))
+    c = _f32(rng.uniform(0.01, 0.05, (H, dv)))
+    S = _f32(rng.normal(0, 0.3, (2, H, dk, dv)))
+    slots = np.array([2, 0], np.int32)
+    orc.store_pool(pool, bits, dk, dv, r, c, slots, S)
+    L = orc.load_pool(pool, bits, dk, dv, r, c, slots)
+    for h in range(H):
+        b = int(bits[h])
+        if b <= 8:
+            s = (r[h][:, None].astype(np.float64) * c[h][None, :]).astype(np.float32).astype(np.float64)
+            Q = 2 ** (b - 1) - 1
+            inr = np.abs(S[:, h]) <= Q * s
+            err = np.abs(L[:, h].astype(np.float64) - S[:, h])
+            assert np.all(err[inr] <= (s / 2 * (1 + 1e-6) + np.zeros_like(err))[inr])
+            assert np.all(np.abs(L[:, h]) <= Q * s * (1 + 1e-6))
+        elif b == 16:
+            assert np.array_equal(L[:, h], S[:, h].astype(np.float16).astype(np.float32))
+        else:
+            assert np.array_equal(L[:, h], S[:, h])
