@@ -151,6 +151,43 @@ def fp32_state_baseline(sq, I, w, dev, stream, ins, quant_ms, steps=16, warmup=1
             "pages_context": "2.91x state-update speedup at 6 bits on NVIDIA A800"}
 
 
+def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, steps=32,
+                      warmup=10):
+    """The per-key-channel-gate (KDA) step, sq_decode_step_kda, on the same pool
+    and inputs with alpha [n_req][H][d_k] resident in HBM: the second model
+    family's step at the same shape.  Reported beside the metric, not in it."""
+    import torch
+
+    ins = []
+    for t in range(n_in):
+        si = I.step_inputs(w, t, dev)
+        si.alpha = I.channel_gates(w, t, dev)
+        ins.append(si)
+    o = torch.empty(w.n_req, w.n_heads, w.dv, device=dev)
+
+    def step(t):
+        x = ins[t % n_in]
+        sq.sq_decode_step_kda(pool, slots, x.q, x.k, x.v, x.alpha, x.beta, o, stream)
+
+    for t in range(warmup):
+        step(t)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for t in range(steps):
+        step(warmup + t)
+        evs[t + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    # the scalar gate's 4 bytes per head-token become 4 d_k bytes
+    byts = algorithmic_bytes_per_step(w, bits) + w.n_req * w.n_heads * 4 * (w.dk - 1)
+    gbps = byts / (ms / 1e3) / 1e9
+    return {"value": w.n_req * w.n_heads / (ms / 1e3), "unit": "heads*tokens/s",
+            "ms_per_step": ms, "hbm_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": byts, "time_vs_scalar_gate_step": ms / quant_ms,
+            "kernel": "k_step128 per-channel-gate instance"}
+
+
 def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
     """The oracle, as it stands, on a bounded sample: whole requests (all 2304
     heads) of the same workload, calibrated to about target_s seconds."""
@@ -195,6 +232,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-baseline", action="store_true",
                     help="skip timing the unquantized FP32-state step at the same shape")
+    ap.add_argument("--no-kda", action="store_true",
+                    help="skip timing the per-key-channel-gate step at the same shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -327,6 +366,12 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+
+    if not args.no_kda:
+        result["channel_gate_step"] = channel_gate_step(sq, I, w, bits, pool, slots, dev, stream,
+                                                        n_in, ms_per_step)
+        log(f"[bench] per-channel-gate step: {result['channel_gate_step']['ms_per_step']:.3f} ms "
+            f"({result['channel_gate_step']['frac']:.3f} of HBM peak)")
 
     if not args.no_fp32_baseline:
         result["fp32_state_baseline"] = fp32_state_baseline(sq, I, w, dev, stream, ins, ms_per_step)

@@ -149,6 +149,21 @@ int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const 
                    const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
                    const float *beta, float *o, void *stream);
 
+/* The same step with a per-key-channel gate, for the second model family
+ * ([P5] 直接量化为什么会翻车 names its gate KDA; the pages give no formula).
+ * Reading taken: the gate is a vector alpha in (0, 1]^{d_k} that decays each
+ * key row of the state before the delta correction,
+ *     T  = diag(alpha) S^,   u = T^T k
+ *     S' = T + beta k (v - u)^T  = (I - beta k k^T) diag(alpha) S^ + beta k v^T
+ *     o  = S'^T q,           tile = encode(S')
+ * which is sq_decode_step when all d_k entries of alpha are equal.  Arguments
+ * as for sq_decode_step except
+ *   alpha    fp32 [n_req][n_heads][d_k], DEVICE, 16-byte aligned.
+ * Same errors; n_req == 0 is a no-op.  Asynchronous on `stream`. */
+int sq_decode_step_kda(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
+                       const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
+                       const float *beta, float *o, void *stream);
+
 /* Readout without update: o = S^T q from the stored state (dequantized), for
  * slots slot_ids[0..n_req).  q: DEVICE [n_req][n_heads][d_k] of q_dtype;
  * o: DEVICE fp32 [n_req][n_heads][d_v].  Does not modify the pool.  n_req == 0

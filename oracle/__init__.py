@@ -73,6 +73,13 @@ def _load():
                                   _f32p, _i32p, ctypes.c_int, _f32p]),
         "orc_load_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
                                  _f32p, _i32p, ctypes.c_int, _f32p]),
+        "orc_step_tile_kda": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
+                                     _f32p, _f32p, _f32p, _f32p, ctypes.c_float, _f32p]),
+        "orc_step_pool_kda": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
+                                     _f32p, _i32p, ctypes.c_int, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                     _f32p, ctypes.c_int]),
+        "orc_bruteforce_kda": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p, _f64p,
+                                      _f64p, _f64p, _f64p, _f64p, _f64p]),
         "orc_bruteforce": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p, _f64p,
                                   _f64p, _f64p, _f64p, _f64p, _f64p]),
     }
@@ -271,4 +278,56 @@ def bruteforce(S0, q, k, v, alpha, beta):
     o = np.empty((T, dv), np.float64)
     _load().orc_bruteforce(dk, dv, T, _p(S0, _f64p), _p(q, _f64p), _p(k, _f64p), _p(v, _f64p),
                            _p(alpha, _f64p), _p(beta, _f64p), _p(ST, _f64p), _p(o, _f64p))
+    return ST, o
+
+
+# ---------------------------------------------------------------- per-channel gate
+
+def step_tile_kda(bits: int, dk: int, dv: int, tile, r, c, q, k, v, alpha, beta: float):
+    """Per-channel-gate step (alpha float32[dk]); returns (new tile, o)."""
+    tile = _c(tile, np.uint8).copy()
+    r, c = _c(r, np.float32), _c(c, np.float32)
+    q, k, v, a = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32), _c(alpha, np.float32)
+    o = np.empty(dv, np.float32)
+    _load().orc_step_tile_kda(bits, dk, dv, _p(tile, _u8p), _p(r, _f32p), _p(c, _f32p),
+                              _p(q, _f32p), _p(k, _f32p), _p(v, _f32p), _p(a, _f32p), float(beta),
+                              _p(o, _f32p))
+    return tile, o
+
+
+def step_pool_kda(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, q, k, v, alpha,
+                  beta, want_o: bool = True, n_threads=None):
+    """Per-channel-gate pool step in place (alpha float32 [n_req][H][dk]); returns o or None."""
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    hb = _c(head_bits, np.uint8)
+    H = hb.size
+    sid = _c(slot_ids, np.int32)
+    n_req = sid.size
+    r, c = _c(r, np.float32), _c(c, np.float32)
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    alpha, beta = _c(alpha, np.float32), _c(beta, np.float32)
+    assert q.size == n_req * H * dk and k.size == n_req * H * dk and v.size == n_req * H * dv
+    assert alpha.size == n_req * H * dk and beta.size == n_req * H
+    assert r.size == H * dk and c.size == H * dv
+    _, slab = pool_layout(hb, dk, dv)
+    assert n_req == 0 or (sid.min() >= 0 and (int(sid.max()) + 1) * slab <= pool.size)
+    o = np.empty((n_req, H, dv), np.float32) if want_o else None
+    _load().orc_step_pool_kda(_p(pool, _u8p), H, dk, dv, _p(hb, _u8p), _p(r, _f32p), _p(c, _f32p),
+                              _p(sid, _i32p), n_req, _p(q, _f32p), _p(k, _f32p), _p(v, _f32p),
+                              _p(alpha, _f32p), _p(beta, _f32p),
+                              _p(o, _f32p) if want_o else None, _threads(n_threads))
+    return o
+
+
+def bruteforce_kda(S0, q, k, v, alpha, beta):
+    """Dense fp64 per-channel-gate recurrence; alpha [T][dk].  Returns (S_T, o[T][dv])."""
+    S0 = _c(S0, np.float64)
+    dk, dv = S0.shape
+    q, k, v = _c(q, np.float64), _c(k, np.float64), _c(v, np.float64)
+    alpha, beta = _c(alpha, np.float64), _c(beta, np.float64)
+    T = beta.size
+    ST = np.empty((dk, dv), np.float64)
+    o = np.empty((T, dv), np.float64)
+    _load().orc_bruteforce_kda(dk, dv, T, _p(S0, _f64p), _p(q, _f64p), _p(k, _f64p), _p(v, _f64p),
+                               _p(alpha, _f64p), _p(beta, _f64p), _p(ST, _f64p), _p(o, _f64p))
     return ST, o

@@ -319,7 +319,12 @@ typedef struct {
     float *o;
     long t0, t1;
     int readout_only;
+    int channel_gate; /* alpha is [n_req][H][d_k] (orc_step_tile_kda) */
 } orc_job;
+
+void orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
+                       const float *q, const float *k, const float *v, const float *alpha,
+                       float beta, float *o);
 
 static void *orc_worker(void *arg)
 {
@@ -334,6 +339,9 @@ static void *orc_worker(void *arg)
         float *o = J->o ? J->o + t * J->dv : NULL;
         if (J->readout_only) {
             orc_readout_tile(J->bits[h], J->dk, J->dv, tile, r, c, q, o);
+        } else if (J->channel_gate) {
+            orc_step_tile_kda(J->bits[h], J->dk, J->dv, tile, r, c, q, J->k + t * J->dk,
+                              J->v + t * J->dv, J->alpha + t * J->dk, J->beta[t], o);
         } else {
             orc_step_tile(J->bits[h], J->dk, J->dv, tile, r, c, q, J->k + t * J->dk,
                           J->v + t * J->dv, J->alpha[t], J->beta[t], o);
@@ -541,4 +549,106 @@ void orc_load_pool(const uint8_t *pool, int n_heads, int dk, int dv, const uint8
         }
     free(D);
     free(off);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-channel gate (the gating of the second model family, Kimi-Linear,     */
+/* named in [P5] 直接量化为什么会翻车 as KDA; the pages give no formula).      */
+/* Reading: the gate is a vector alpha in R^{d_k} that decays each key row,  */
+/*     S' = (I - beta k k^T) diag(alpha) S + beta k v^T.                      */
+/* With T = diag(alpha) S and u = T^T k:  S'_ij = alpha_i S_ij               */
+/*     + beta k_i (v_j - u_j),  o = S'^T q.                                  */
+/* ------------------------------------------------------------------------ */
+
+void orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
+                       const float *q, const float *k, const float *v, const float *alpha,
+                       float beta, float *o)
+{
+    double *S = (double *)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+    double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+    orc_decode_tile(bits, dk, dv, tile, r, c, S);
+    for (int i = 0; i < dk; i++)
+        for (int j = 0; j < dv; j++) S[(long)i * dv + j] *= (double)alpha[i]; /* T */
+    for (int j = 0; j < dv; j++) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; i++) acc += (double)k[i] * S[(long)i * dv + j];
+        u[j] = acc;
+    }
+    double b = beta;
+    for (int i = 0; i < dk; i++)
+        for (int j = 0; j < dv; j++) S[(long)i * dv + j] += b * (double)k[i] * ((double)v[j] - u[j]);
+    if (o) {
+        for (int j = 0; j < dv; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; i++) acc += (double)q[i] * S[(long)i * dv + j];
+            o[j] = (float)acc;
+        }
+    }
+    orc_encode_tile(bits, dk, dv, S, r, c, tile);
+    free(u);
+    free(S);
+}
+
+/* Pool-level per-channel-gate step; alpha is [n_req][H][d_k], the rest as
+ * orc_step_pool. */
+void orc_step_pool_kda(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
+                       const float *r, const float *c, const int32_t *slot_ids, int n_req,
+                       const float *q, const float *k, const float *v, const float *alpha,
+                       const float *beta, float *o, int n_threads)
+{
+    int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
+    orc_job J;
+    memset(&J, 0, sizeof(J));
+    J.pool = pool;
+    J.slab = orc_pool_layout(n_heads, head_bits, dk, dv, off);
+    J.off = off;
+    J.n_heads = n_heads;
+    J.dk = dk;
+    J.dv = dv;
+    J.bits = head_bits;
+    J.r = r;
+    J.c = c;
+    J.slot_ids = slot_ids;
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.alpha = alpha;
+    J.beta = beta;
+    J.o = o;
+    J.channel_gate = 1;
+    orc_run(&J, (long)n_req * n_heads, n_threads);
+    free(off);
+}
+
+/* Dense fp64 recurrence with A_t = (I - beta_t k_t k_t^T) diag(alpha_t);
+ * alpha is [T][d_k].  Same conventions as orc_bruteforce. */
+void orc_bruteforce_kda(int dk, int dv, int T, const double *S0, const double *q, const double *k,
+                        const double *v, const double *alpha, const double *beta, double *ST,
+                        double *o)
+{
+    size_t kk = (size_t)dk * dk, kv = (size_t)dk * dv;
+    double *A = (double *)malloc(sizeof(double) * kk);
+    double *St = (double *)malloc(sizeof(double) * kv);
+    double *nx = (double *)malloc(sizeof(double) * kv);
+    memcpy(St, S0, sizeof(double) * kv);
+    for (int t = 0; t < T; t++) {
+        for (int i = 0; i < dk; i++)
+            for (int l = 0; l < dk; l++)
+                A[(size_t)i * dk + l] = ((i == l ? 1.0 : 0.0) - beta[t] * k[(long)t * dk + i] *
+                                         k[(long)t * dk + l]) * alpha[(long)t * dk + l];
+        matmul(dk, dk, dv, A, St, nx);
+        for (int i = 0; i < dk; i++)
+            for (int j = 0; j < dv; j++)
+                nx[(long)i * dv + j] += beta[t] * k[(long)t * dk + i] * v[(long)t * dv + j];
+        memcpy(St, nx, sizeof(double) * kv);
+        for (int j = 0; j < dv; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; i++) acc += q[(long)t * dk + i] * St[(long)i * dv + j];
+            o[(long)t * dv + j] = acc;
+        }
+    }
+    memcpy(ST, St, sizeof(double) * kv);
+    free(nx);
+    free(St);
+    free(A);
 }

@@ -5,7 +5,8 @@
 // Sources: [P1] "K1 論文詳解" (k1-news, 2026-10-09), 背景 / 方法;
 //          [P5] "线性注意力状态量化难题:Qwen状态池70并发就超模型权重" (aitest123),
 //          opening (one resident state per concurrent request), 时间维度
-//          (per-head bit widths, FP16 pivots), 空间维度 (row x column factors).
+//          (per-head bit widths, FP16 pivots), 空间维度 (row x column factors),
+//          直接量化为什么会翻车 (the KDA gate of the second model family).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -194,7 +195,8 @@ static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16,
     // d = 128: one launch over all tiles in pool order; otherwise one launch
     // per width class, widest tiles first
     static const int order[5] = {4, 3, 2, 1, 0};
-    if ((op == sqk::OP_STEP || op == sqk::OP_READOUT) && p->dk == 128 && p->dv == 128) {
+    const bool step_or_read = op == sqk::OP_STEP || op == sqk::OP_STEP_KDA || op == sqk::OP_READOUT;
+    if (step_or_read && p->dk == 128 && p->dv == 128) {
         const uint64_t total = (uint64_t)n_req * (uint64_t)p->n_heads;
         if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
         if (p->n_class[4] < p->n_heads) {  // any 4/6/8/16-bit heads
@@ -264,6 +266,28 @@ int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const 
     a.beta = beta;
     a.o = o;
     return run_classes(pool, sqk::OP_STEP, a, qkv_dtype == SQ_BF16, n_req, stream);
+}
+
+int sq_decode_step_kda(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
+                       const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
+                       const float *beta, float *o, void *stream)
+{
+    if (!pool || n_req < 0) return SQ_ERR_INVALID;
+    if (qkv_dtype != SQ_F32 && qkv_dtype != SQ_BF16) return SQ_ERR_INVALID;
+    if (n_req == 0) return SQ_OK;
+    if (n_req > pool->n_slots || !slot_ids || !q || !k || !v || !alpha || !beta)
+        return SQ_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
+        (o && !aligned(o, 16)))
+        return SQ_ERR_INVALID;
+    sqk::StepArgs a = base_args(pool, slot_ids);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.o = o;
+    return run_classes(pool, sqk::OP_STEP_KDA, a, qkv_dtype == SQ_BF16, n_req, stream);
 }
 
 int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,

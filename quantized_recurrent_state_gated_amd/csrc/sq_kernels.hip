@@ -24,6 +24,7 @@
 // n = q + 2^(b-1); the bias is folded into per-tile constants.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "sq_launch.h"
@@ -275,8 +276,14 @@ struct Smem128 {
     float sum[2][3];               // per-wave partials of q.k, sum w, sum g
 };
 
-template <int BITS, typename T, bool UPDATE>
-__device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, Smem128 &sm)
+// Per-key-channel gate: pass 2 needs a per-row gate.  pa[i] = {beta k_i / r_i,
+// alpha_i 2^-s0, alpha_i 2^-s1, OFF (1 - alpha_i)}.
+struct Smem128K : Smem128 {
+    alignas(16) float4 pa[128];
+};
+
+template <int BITS, typename T, bool UPDATE, bool CHG, typename SM>
+__device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM &sm)
 {
     constexpr int W = BITS / 2;
     constexpr bool QUANT = BITS <= 8;
@@ -300,7 +307,9 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, Sm
 #pragma unroll
     for (int m = 0; m < 4; m++) load_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
 
-    const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
+    // with a per-channel gate alpha_i multiplies row i of the weights and the
+    // column terms take alpha = 1: u = (diag(alpha) S)^T k, o = y + beta (q.k) (v - u)
+    const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
     const float beta = UPDATE ? a.beta[nh] : 0.0f;
 
     // per-row factors (threads 0..127, one row each) and the three tile sums
@@ -308,10 +317,13 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, Sm
         const float qi = ld1(q, nh * 128 + t);
         const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
         const float ri = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
-        const float wi = ki * ri, gi = qi * ri;
+        const float gate = CHG ? a.alpha[nh * 128 + t] : 1.0f;
+        const float wi = ki * ri * gate, gi = qi * ri * gate;
         sm.w[t] = wi;
         sm.g[t] = gi;
-        if (UPDATE) sm.a[t] = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        if constexpr (CHG) sm.pa[t] = make_float4(ai, gate, gate, OFF * (1.0f - gate));
+        else if (UPDATE) sm.a[t] = ai;
         const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
         if ((t & 63) == 0) {
             sm.sum[t >> 6][0] = s0;
@@ -378,10 +390,17 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, Sm
         float z[16];
 #pragma unroll
         for (int ri = 0; ri < 4; ri++) {
-            const float ai = sm.a[i0 + ri];
+            if constexpr (CHG) {
+                const float4 p = sm.pa[i0 + ri];
 #pragma unroll
-            for (int cj = 0; cj < 4; cj++)
-                z[4 * cj + ri] = fmaf(alpha, f[m][4 * cj + ri], fmaf(ai, b[cj], C));
+                for (int cj = 0; cj < 4; cj++)
+                    z[4 * cj + ri] = fmaf(p.y, f[m][4 * cj + ri], fmaf(p.x, b[cj], p.w));
+            } else {
+                const float ai = sm.a[i0 + ri];
+#pragma unroll
+                for (int cj = 0; cj < 4; cj++)
+                    z[4 * cj + ri] = fmaf(alpha, f[m][4 * cj + ri], fmaf(ai, b[cj], C));
+            }
         }
         uint32_t dn[W];
         encode<BITS>(z, dn);
@@ -478,8 +497,8 @@ __device__ __forceinline__ float half_of(uint32_t x, int sel)
     return sel ? __high2float(hh) : __low2float(hh);
 }
 
-template <int BITS, typename T, bool UPDATE, int TPB>
-__device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128 &sm)
+template <int BITS, typename T, bool UPDATE, bool CHG, int TPB, typename SM>
+__device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
 {
     // TPB threads per tile: RG = TPB / 32 row groups, MB = 32 / RG blocks per thread
     constexpr int RG = TPB / 32, MB = 32 / RG;
@@ -514,16 +533,21 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
         for (int m = 0; m < MB; m++) to_halves<BITS>(d[m], hv[m]);
     }
 
-    const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
+    // per-channel gate: alpha_i scales row i of the weights, the column terms
+    // take alpha = 1 (u = (diag(alpha) S)^T k, o = y + beta (q.k) (v - u))
+    const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
     const float beta = UPDATE ? a.beta[nh] : 0.0f;
 
     if (t < 128) {
         const float qi = ld1(q, nh * 128 + t);
         const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
         const float ri = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
-        const float wi = ki * ri, gi = qi * ri;
+        const float gate = CHG ? a.alpha[nh * 128 + t] : 1.0f;
+        const float wi = ki * ri * gate, gi = qi * ri * gate;
         sm.wg[t] = make_float4(wi * SC0, wi * SC1, gi * SC0, gi * SC1);
-        if (UPDATE) sm.a[t] = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        if constexpr (CHG) sm.pa[t] = make_float4(ai, gate * SC0, gate * SC1, OFF * (1.0f - gate));
+        else if (UPDATE) sm.a[t] = ai;
         const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
         if ((t & 63) == 0) {
             sm.sum[t >> 6][0] = s0;
@@ -599,12 +623,22 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
         float z[16];
 #pragma unroll
         for (int ri = 0; ri < 4; ri++) {
-            const float ai = sm.a[i0 + ri];
+            if constexpr (CHG) {
+                const float4 p = sm.pa[i0 + ri];
 #pragma unroll
-            for (int cj = 0; cj < 4; cj++) {
-                const int e = 4 * cj + ri;
-                const float x = half_of(hv[m][P::k(e)], P::sel(e));
-                z[e] = fmaf(P::cls(e) ? al1 : al0, x, fmaf(ai, b[cj], C));
+                for (int cj = 0; cj < 4; cj++) {
+                    const int e = 4 * cj + ri;
+                    const float x = half_of(hv[m][P::k(e)], P::sel(e));
+                    z[e] = fmaf(P::cls(e) ? p.z : p.y, x, fmaf(p.x, b[cj], p.w));
+                }
+            } else {
+                const float ai = sm.a[i0 + ri];
+#pragma unroll
+                for (int cj = 0; cj < 4; cj++) {
+                    const int e = 4 * cj + ri;
+                    const float x = half_of(hv[m][P::k(e)], P::sel(e));
+                    z[e] = fmaf(P::cls(e) ? al1 : al0, x, fmaf(ai, b[cj], C));
+                }
             }
         }
         uint32_t dn[W];
@@ -613,33 +647,35 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, Smem128
     }
 }
 
-template <typename T, bool UPDATE, int TPB, int WPE>
+template <typename T, bool UPDATE, bool CHG, int TPB, int WPE>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void k_step128(FusedArgs f)
 {
     // block b is request b / H, head b % H: the grid walks the pool in memory
     // order, so tiles of every width are interleaved on each CU (VALU-heavy
     // narrow codes overlap with memory-heavy wide tiles).  FP32 heads are
     // skipped here and run in k_step128_f32.
-    __shared__ Smem128 sm;
+    using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
+    __shared__ SM sm;
     const uint32_t b = blockIdx.x;
     const int n = (int)(b / (uint32_t)f.a.H);
     const int h = (int)(b - (uint32_t)n * (uint32_t)f.a.H);
     switch (f.head_bits[h]) {
-    case 16: tile128<16, T, UPDATE, TPB>(f.a, n, h, sm); break;
-    case 8: tile128<8, T, UPDATE, TPB>(f.a, n, h, sm); break;
-    case 6: tile128<6, T, UPDATE, TPB>(f.a, n, h, sm); break;
-    case 4: tile128<4, T, UPDATE, TPB>(f.a, n, h, sm); break;
+    case 16: tile128<16, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
+    case 8: tile128<8, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
+    case 6: tile128<6, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
+    case 4: tile128<4, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
     default: break;
     }
 }
 
-template <typename T, bool UPDATE>
+template <typename T, bool UPDATE, bool CHG>
 __global__ __launch_bounds__(256) void k_step128_f32(StepArgs a)
 {
-    __shared__ Smem128 sm;
+    using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
+    __shared__ SM sm;
     const int n = blockIdx.x / a.Hc;
     const int h = a.heads[blockIdx.x - n * a.Hc];
-    tile128_wide<32, T, UPDATE>(a, n, h, sm);
+    tile128_wide<32, T, UPDATE, CHG>(a, n, h, sm);
 }
 
 // ---------------------------------------------------------------- any shape
@@ -669,13 +705,13 @@ __device__ __forceinline__ float field_value(uint32_t f)
     else return __uint_as_float(f);
 }
 
-template <int BITS, typename T, bool UPDATE>
+template <int BITS, typename T, bool UPDATE, bool CHG>
 __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
 {
     constexpr int W = BITS / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
-    __shared__ float sW[256], sG[256], sA[256], sB[256];
+    __shared__ float sW[256], sG[256], sA[256], sB[256], sL[256];
     __shared__ float sQK;
 
     const int t = threadIdx.x;
@@ -688,15 +724,18 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
     const T *q = reinterpret_cast<const T *>(a.q);
     const T *k = reinterpret_cast<const T *>(a.k);
     const T *v = reinterpret_cast<const T *>(a.v);
-    const float alpha = UPDATE ? a.alpha[nh] : 1.0f;
+    // per-channel gate: row i is scaled by alpha_i and the column terms take alpha = 1
+    const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
     const float beta = UPDATE ? a.beta[nh] : 0.0f;
 
     for (int i = t; i < dk; i += 256) {
         const float ri = QUANT ? a.rsc[(long)h * dk + i] : 1.0f;
         const float ki = UPDATE ? ld1(k, nh * dk + i) : 0.0f;
-        sW[i] = ki * ri;
-        sG[i] = ld1(q, nh * dk + i) * ri;
+        const float gate = CHG ? a.alpha[nh * dk + i] : alpha;
+        sW[i] = ki * ri * (CHG ? gate : 1.0f);
+        sG[i] = ld1(q, nh * dk + i) * ri * (CHG ? gate : 1.0f);
         sA[i] = QUANT ? beta * ki / ri : beta * ki;
+        sL[i] = gate;
     }
     if (t == 0) {
         float s = 0.0f;
@@ -724,7 +763,6 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
     }
     if (!UPDATE) return;
     __syncthreads();
-    const float C = OFF * (1.0f - alpha);
     const int nblk = (dk >> 2) * (dv >> 2);
     for (int B = t; B < nblk; B += 256) {
         const int i0 = 4 * (B / (dv >> 2)), j0 = 4 * (B % (dv >> 2));
@@ -737,8 +775,10 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
 #pragma unroll
         for (int cj = 0; cj < 4; cj++)
 #pragma unroll
-            for (int ri = 0; ri < 4; ri++)
-                z[4 * cj + ri] = fmaf(alpha, f[4 * cj + ri], fmaf(sA[i0 + ri], sB[j0 + cj], C));
+            for (int ri = 0; ri < 4; ri++) {
+                const float g = sL[i0 + ri];
+                z[4 * cj + ri] = fmaf(g, f[4 * cj + ri], fmaf(sA[i0 + ri], sB[j0 + cj], OFF * (1.0f - g)));
+            }
         encode<BITS>(z, dd);
         uint32_t *dst = reinterpret_cast<uint32_t *>(tile + (long)B * 2 * BITS);
 #pragma unroll
@@ -852,9 +892,11 @@ static hipError_t launch_bits(Op op, const StepArgs &a, int32_t n_req, hipStream
     }
     const dim3 grid((unsigned)((long)n_req * a.Hc));
     if (op == OP_STEP)
-        hipLaunchKernelGGL((k_tile_any<BITS, T, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_tile_any<BITS, T, true, false>), grid, dim3(256), 0, st, a);
+    else if (op == OP_STEP_KDA)
+        hipLaunchKernelGGL((k_tile_any<BITS, T, true, true>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_tile_any<BITS, T, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_tile_any<BITS, T, false, false>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -871,38 +913,42 @@ static hipError_t launch_t(Op op, int bits, const StepArgs &a, int32_t n_req, hi
     }
 }
 
+template <typename T>
+static void f32_128_t(Op op, const StepArgs &a, dim3 grid, hipStream_t st)
+{
+    if (op == OP_STEP)
+        hipLaunchKernelGGL((k_step128_f32<T, true, false>), grid, dim3(256), 0, st, a);
+    else if (op == OP_STEP_KDA)
+        hipLaunchKernelGGL((k_step128_f32<T, true, true>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_step128_f32<T, false, false>), grid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_f32_128(Op op, bool qkv_bf16, const StepArgs &a, int32_t n_req, hipStream_t st)
 {
     if (n_req <= 0 || a.Hc <= 0) return hipSuccess;
     const dim3 grid((unsigned)((long)n_req * a.Hc));
-    if (op == OP_STEP) {
-        if (qkv_bf16)
-            hipLaunchKernelGGL((k_step128_f32<uint16_t, true>), grid, dim3(256), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_step128_f32<float, true>), grid, dim3(256), 0, st, a);
-    } else {
-        if (qkv_bf16)
-            hipLaunchKernelGGL((k_step128_f32<uint16_t, false>), grid, dim3(256), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_step128_f32<float, false>), grid, dim3(256), 0, st, a);
-    }
+    if (qkv_bf16) f32_128_t<uint16_t>(op, a, grid, st);
+    else f32_128_t<float>(op, a, grid, st);
     return hipGetLastError();
+}
+
+template <typename T, int TPB, int WPE>
+static void fused128_t(Op op, const FusedArgs &f, dim3 grid, hipStream_t st)
+{
+    if (op == OP_STEP)
+        hipLaunchKernelGGL((k_step128<T, true, false, TPB, WPE>), grid, dim3(TPB), 0, st, f);
+    else if (op == OP_STEP_KDA)
+        hipLaunchKernelGGL((k_step128<T, true, true, TPB, WPE>), grid, dim3(TPB), 0, st, f);
+    else
+        hipLaunchKernelGGL((k_step128<T, false, false, TPB, WPE>), grid, dim3(TPB), 0, st, f);
 }
 
 template <int TPB, int WPE>
 static void fused128(Op op, bool qkv_bf16, const FusedArgs &f, dim3 grid, hipStream_t st)
 {
-    if (op == OP_STEP) {
-        if (qkv_bf16)
-            hipLaunchKernelGGL((k_step128<uint16_t, true, TPB, WPE>), grid, dim3(TPB), 0, st, f);
-        else
-            hipLaunchKernelGGL((k_step128<float, true, TPB, WPE>), grid, dim3(TPB), 0, st, f);
-    } else {
-        if (qkv_bf16)
-            hipLaunchKernelGGL((k_step128<uint16_t, false, TPB, WPE>), grid, dim3(TPB), 0, st, f);
-        else
-            hipLaunchKernelGGL((k_step128<float, false, TPB, WPE>), grid, dim3(TPB), 0, st, f);
-    }
+    if (qkv_bf16) fused128_t<uint16_t, TPB, WPE>(op, f, grid, st);
+    else fused128_t<float, TPB, WPE>(op, f, grid, st);
 }
 
 hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,

@@ -20,12 +20,14 @@ struct StepArgs {
     const float *rsc;          // [H][dk]
     const float *csc;          // [H][dv]
     const void *q, *k, *v;     // [n_req][H][d]
-    const float *alpha, *beta; // [n_req][H]
+    const float *alpha;        // [n_req][H]; per-channel gate: [n_req][H][dk]
+    const float *beta;         // [n_req][H]
     float *o;                  // [n_req][H][dv] or null
     const float *S;            // store: source, load: destination, [n_req][H][dk][dv]
 };
 
-enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2, OP_LOAD = 3 };
+// OP_STEP_KDA is the step with a per-key-channel gate (alpha [n_req][H][dk]).
+enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2, OP_LOAD = 3, OP_STEP_KDA = 4 };
 
 // One launch over every tile of a d_k = d_v = 128 pool: block b is request
 // b / H, head b % H, whose width is head_bits[h].

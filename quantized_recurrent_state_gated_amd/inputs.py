@@ -275,6 +275,27 @@ def step_inputs(w: Workload, t: int, device="cpu") -> StepInputs:
                       alpha.contiguous(), beta.contiguous())
 
 
+def channel_gates(w: Workload, t: int, device="cpu") -> torch.Tensor:
+    """Per-key-channel gates alpha [n_req][H][d_k] of decode step t, for the
+    per-channel (KDA) step; q, k, v and beta come from step_inputs.
+
+    tiny: alpha = exp(-softplus(a)), a ~ N(0, 1) per channel.  Otherwise
+    ln alpha_i = -(ln 2 / h) exp(0.5 z + 0.5 z_i - 0.25), z ~ N(0, 1) per
+    (request, head) and z_i ~ N(0, 1) per channel: every channel decays at its
+    own rate around the head's half-life h, with the head's mean
+    log-retention -ln2/h as in step_inputs ([P5] 时间维度)."""
+    gen = _torch_gen(w, 1_000_000_000 + t, device)
+    n, H = w.n_req, w.n_heads
+    f32 = torch.float32
+    zc = torch.randn(n, H, w.dk, generator=gen, device=device, dtype=f32)
+    if w.tiny_recipe:
+        return torch.exp(-torch.nn.functional.softplus(zc)).contiguous()
+    z = torch.randn(n, H, 1, generator=gen, device=device, dtype=f32)
+    h = torch.from_numpy(half_lives(w).astype(np.float32)).to(device)
+    rate = (math.log(2.0) / h)[None, :, None]
+    return torch.exp(-rate * torch.exp(0.5 * z + 0.5 * zc - 0.25)).contiguous()
+
+
 def pool_stats(w: Workload) -> dict:
     """Sizes of the workload's pool and per-step traffic at the layout's tile sizes."""
     bits = head_bits(w)

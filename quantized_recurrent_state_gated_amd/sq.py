@@ -25,7 +25,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM = 0, -1, -2, -3, -4
 SQ_F32, SQ_BF16 = 0, 1
 EXPORTED = ("sq_pool_bytes", "sq_pool_alloc", "sq_pool_free", "sq_pool_tile_offset",
-            "sq_pool_store", "sq_pool_load", "sq_decode_step", "sq_readout", "sq_status_string")
+            "sq_pool_store", "sq_pool_load", "sq_decode_step", "sq_decode_step_kda", "sq_readout",
+            "sq_status_string")
 
 
 class SqPoolDesc(ctypes.Structure):
@@ -52,6 +53,8 @@ _lib.sq_pool_load.restype = ctypes.c_int
 _lib.sq_pool_load.argtypes = [_vp, _vp, _i32, _vp, _vp]
 _lib.sq_decode_step.restype = ctypes.c_int
 _lib.sq_decode_step.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
+_lib.sq_decode_step_kda.restype = ctypes.c_int
+_lib.sq_decode_step_kda.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
 _lib.sq_readout.restype = ctypes.c_int
 _lib.sq_readout.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp]
 _lib.sq_status_string.restype = ctypes.c_char_p
@@ -172,6 +175,16 @@ def sq_decode_step(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=
     _check(_lib.sq_decode_step(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _ptr(k), _ptr(v),
                                _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream)),
            "sq_decode_step")
+
+
+def sq_decode_step_kda(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=None) -> None:
+    """Per-key-channel-gate step; alpha is fp32 [n_req][n_heads][d_k]."""
+    n_req = int(slot_ids.numel())
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    _check(_lib.sq_decode_step_kda(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _ptr(k), _ptr(v),
+                                   _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(o),
+                                   _stream(stream)), "sq_decode_step_kda")
 
 
 def sq_readout(pool: SqPool, slot_ids, q, o, stream=None) -> None:

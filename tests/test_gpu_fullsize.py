@@ -72,7 +72,7 @@ def check_store(orc, dp, tiles):
             assert np.array_equal(g, want), f"store tile ({n}, {h}) bits {dp.bits[h]}"
 
 
-def check_step(orc, dp, tiles, si, pre, post, o, tally):
+def check_step(orc, dp, tiles, si, pre, post, o, tally, kda=False):
     w = dp.w
     q, k, v = host_f32(si.q), host_f32(si.k), host_f32(si.v)
     al, be = si.alpha.cpu().numpy(), si.beta.cpu().numpy()
@@ -80,9 +80,9 @@ def check_step(orc, dp, tiles, si, pre, post, o, tally):
 
     def one(i):
         n, h = tiles[i]
-        t, oo = orc.step_tile(int(dp.bits[h]), w.dk, w.dv, pre[i], dp.rh[h], dp.ch[h], q[n, h],
-                              k[n, h], v[n, h], al[n, h], be[n, h])
-        return t, oo
+        step = orc.step_tile_kda if kda else orc.step_tile
+        return step(int(dp.bits[h]), w.dk, w.dv, pre[i], dp.rh[h], dp.ch[h], q[n, h], k[n, h],
+                    v[n, h], al[n, h], be[n, h])
 
     with cf.ThreadPoolExecutor(THREADS) as ex:
         res = list(ex.map(one, range(len(tiles))))
@@ -92,9 +92,10 @@ def check_step(orc, dp, tiles, si, pre, post, o, tally):
     tally.add_o(np.stack([o_gpu[n, h] for n, h in tiles]), np.stack([r[1] for r in res]))
 
 
-def run_fullsize(sq, orc, name, check_steps, n_random=2048, all_tiles_at=()):
+def run_fullsize(sq, orc, name, check_steps, n_random=2048, all_tiles_at=(), kda=False):
+    """kda: step with sq_decode_step_kda and per-channel gates I.channel_gates."""
     w = I.WORKLOADS[name]
-    say(f"[{name}] init {w.n_req} x {w.n_heads}")
+    say(f"[{name}{' kda' if kda else ''}] init {w.n_req} x {w.n_heads}")
     dp = DevicePool(sq, w)
     rng = np.random.default_rng(7)
     tiles = sample(w, dp.bits, rng, n_random)
@@ -105,15 +106,18 @@ def run_fullsize(sq, orc, name, check_steps, n_random=2048, all_tiles_at=()):
     every = [(n, h) for n in range(w.n_req) for h in range(w.n_heads)]
     for t in range(max(check_steps) + 1):
         si = I.step_inputs(w, t, "cuda")
+        if kda:
+            si.alpha = I.channel_gates(w, t, "cuda")
         check = t in check_steps
         sel = every if t in all_tiles_at else tiles
         if check:
             pre = dp.tile_bytes(sel)
-        sq.sq_decode_step(dp.pool, dp.slots, si.q, si.k, si.v, si.alpha, si.beta, o)
+        step = sq.sq_decode_step_kda if kda else sq.sq_decode_step
+        step(dp.pool, dp.slots, si.q, si.k, si.v, si.alpha, si.beta, o)
         if check:
             torch.cuda.synchronize()
             post = dp.tile_bytes(sel)
-            check_step(orc, dp, sel, si, pre, post, o, tally)
+            check_step(orc, dp, sel, si, pre, post, o, tally, kda)
             say(f"[{name}] step {t} ({len(sel)} tiles): {tally.summary()}")
     tally.check()
 
@@ -131,3 +135,8 @@ def test_drift_full_length(sq, orc):
     tiles every 128 steps."""
     steps = tuple(range(0, 2048, 128)) + (1, 1024, 2047)
     run_fullsize(sq, orc, "drift", check_steps=steps, n_random=256, all_tiles_at=(0, 1, 1024, 2047))
+
+
+def test_serving_full_size_channel_gate(sq, orc):
+    """The per-key-channel-gate step at the serving size, in the launch bench.py times."""
+    run_fullsize(sq, orc, "serving", check_steps=(0, 1, 31), kda=True)

@@ -8,88 +8,16 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import Tally, compare_pools, host_f32, say, unpack_fields
+from gpu_harness import Case, Tally, host_f32, run_teacher_forced, say, unpack_fields
 from quantized_recurrent_state_gated_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
-
-ORACLE_THREADS = 16
 
 
 @pytest.fixture(scope="module")
 def sq():
     from quantized_recurrent_state_gated_amd import sq as m
     return m
-
-
-class Case:
-    """A pool on the GPU initialised from the oracle's quantize-and-store."""
-
-    def __init__(self, sq, orc, w, n_slots=None, slots=None, bits=None, scales=None, S0=None):
-        self.sq, self.orc, self.w = sq, orc, w
-        self.bits = np.asarray(I.head_bits(w) if bits is None else bits, np.uint8)
-        H, dk, dv = w.n_heads, w.dk, w.dv
-        if scales is None:
-            r, c = I.scales(w)
-            r, c = r.numpy(), c.numpy()
-        else:
-            r, c = scales
-        self.r, self.c = np.ascontiguousarray(r, np.float32), np.ascontiguousarray(c, np.float32)
-        self.off, self.slab = orc.pool_layout(self.bits, dk, dv)
-        self.n_slots = n_slots or w.n_req
-        self.slots = np.arange(w.n_req, dtype=np.int32) if slots is None else np.asarray(slots, np.int32)
-        host = np.zeros(self.n_slots * self.slab, np.uint8)
-        if S0 is None:
-            S0 = torch.stack([I.initial_state(w, p) for p in range(w.n_req)]).numpy()
-        self.S0 = np.ascontiguousarray(S0, np.float32)
-        orc.store_pool(host, self.bits, dk, dv, self.r, self.c, self.slots, self.S0)
-        self.dev = torch.from_numpy(host).cuda()
-        self.rd = torch.from_numpy(self.r).cuda()
-        self.cd = torch.from_numpy(self.c).cuda()
-        self.pool = sq.sq_pool_alloc(self.n_slots, H, dk, dv, self.bits, self.rd, self.cd, self.dev)
-        self.slots_d = torch.from_numpy(self.slots).cuda()
-
-    def host(self):
-        torch.cuda.synchronize()
-        return self.dev.cpu().numpy()
-
-    def step(self, si, want_o=True):
-        w = self.w
-        o = torch.empty(w.n_req, w.n_heads, w.dv, device="cuda") if want_o else None
-        self.sq.sq_decode_step(self.pool, self.slots_d, si.q.cuda(), si.k.cuda(), si.v.cuda(),
-                               si.alpha.cuda(), si.beta.cuda(), o)
-        return o
-
-    def oracle_step(self, pre, si):
-        ref = pre.copy()
-        o = self.orc.step_pool(ref, self.bits, self.w.dk, self.w.dv, self.r, self.c, self.slots,
-                               host_f32(si.q), host_f32(si.k), host_f32(si.v), host_f32(si.alpha),
-                               host_f32(si.beta), n_threads=ORACLE_THREADS)
-        return ref, o
-
-    def compare(self, tally, post, ref):
-        compare_pools(tally, post, ref, self.bits, self.off, self.slab, self.slots, self.w.dk,
-                      self.w.dv)
-
-
-def run_teacher_forced(case, steps, label, check_changes=True):
-    tally = Tally()
-    changed = 0
-    for t in range(steps):
-        si = I.step_inputs(case.w, t)
-        pre = case.host()
-        o = case.step(si)
-        post = case.host()
-        ref, o_ref = case.oracle_step(pre, si)
-        case.compare(tally, post, ref)
-        tally.add_o(o.cpu().numpy(), o_ref)
-        changed += int((post != pre).any())
-        if t % 32 == 0 or t == steps - 1:
-            say(f"[{label}] step {t}: {tally.summary()}")
-    tally.check()
-    if check_changes:
-        assert changed == steps  # every step moved the state
-    return tally
 
 
 # ------------------------------------------------------------------ store

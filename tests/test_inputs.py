@@ -95,3 +95,20 @@ def test_spearman_helper_matches_scipy():
     b = a + rng.standard_normal(200)
     b[:20] = b[0]  # ties
     assert abs(spearman(a, b) - spearmanr(a, b).correlation) < 1e-12
+
+
+def test_channel_gates_distribution():
+    w = I.WORKLOADS["layer"]
+    a = I.channel_gates(w, 3)
+    assert a.shape == (w.n_req, w.n_heads, w.dk) and a.dtype == torch.float32
+    assert float(a.max()) <= 1.0 and float(a.min()) > 0.0
+    # channels of one head differ; their mean log-retention is the head's -ln2/h
+    assert float(a.std(dim=-1).min()) > 0
+    hl = I.half_lives(w)
+    la = torch.stack([torch.log(I.channel_gates(w, t)) for t in range(50)]).double()
+    est = -la.mean(dim=(0, 1, 3)).numpy() * hl / math.log(2)
+    assert abs(float(np.median(est)) - 1) < 0.05
+    assert torch.equal(I.channel_gates(w, 3), a)
+    assert not torch.equal(I.channel_gates(w, 4), a)
+    t = I.channel_gates(I.WORKLOADS["tiny"], 0)
+    assert t.shape == (1, 4, 16) and float(t.max()) < 1.0

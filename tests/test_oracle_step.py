@@ -378,3 +378,111 @@ def test_load_after_store_is_within_half_a_step(orc):
             assert np.array_equal(L[:, h], S[:, h].astype(np.float16).astype(np.float32))
         else:
             assert np.array_equal(L[:, h], S[:, h])
+
+
+# ------------------------------------------------------------ per-channel gate
+
+def test_kda_one_step_exact_rational(orc):
+    rng = np.random.default_rng(100)
+    dk, dv = 4, 5
+    S = _f32(rng.standard_normal((dk, dv)))
+    q, k = _f32(rng.standard_normal(dk)), _f32(rng.standard_normal(dk))
+    v = _f32(rng.standard_normal(dv))
+    a = _f32(rng.uniform(0.3, 1.0, dk))
+    beta = np.float32(0.625)
+    tile, r1, c1 = _fp32_tile(orc, S.astype(np.float64))
+    nt, o = orc.step_tile_kda(32, dk, dv, tile, r1, c1, q, k, v, a, beta)
+    Sn = orc.decode_tile(32, dk, dv, nt, r1, c1)
+    Sf = [[F(float(S[i, j])) for j in range(dv)] for i in range(dk)]
+    kf, qf, vf, af = ([F(float(x)) for x in y] for y in (k, q, v, a))
+    b = F(float(beta))
+    A = [[((1 if i == l else 0) - b * kf[i] * kf[l]) * af[l] for l in range(dk)] for i in range(dk)]
+    Sx = [[sum(A[i][l] * Sf[l][j] for l in range(dk)) + b * kf[i] * vf[j] for j in range(dv)]
+          for i in range(dk)]
+    for i in range(dk):
+        for j in range(dv):
+            assert Sn[i, j] == float(np.float32(float(Sx[i][j])))
+    ox = [sum(qf[i] * Sx[i][j] for i in range(dk)) for j in range(dv)]
+    for j in range(dv):
+        assert abs(float(o[j]) - float(ox[j])) <= 2 ** -23 * abs(float(ox[j])) + 1e-30
+
+
+def test_kda_matches_bruteforce_and_reduces_to_scalar_gate(orc):
+    rng = np.random.default_rng(101)
+    dk, dv, T = 16, 12, 6
+    S0 = _f32(rng.normal(0, 0.2, (dk, dv))).astype(np.float64)
+    q, k = _f32(_unit(rng, T, dk)), _f32(_unit(rng, T, dk))
+    v = _f32(rng.standard_normal((T, dv)))
+    a = _f32(rng.uniform(0.5, 1.0, (T, dk)))
+    beta = _f32(rng.uniform(0, 1, T))
+    ST, o_ref = orc.bruteforce_kda(S0, q, k, v, a, beta)
+    tile, r1, c1 = _fp32_tile(orc, S0)
+    for t in range(T):
+        tile, o = orc.step_tile_kda(32, dk, dv, tile, r1, c1, q[t], k[t], v[t], a[t], beta[t])
+        np.testing.assert_allclose(o, o_ref[t], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(orc.decode_tile(32, dk, dv, tile, r1, c1), ST, rtol=1e-5, atol=1e-6)
+    # every channel equal: the scalar gated delta rule (dense form, separate code)
+    a_s = _f32(rng.uniform(0.5, 1.0, T))
+    ST1, o1 = orc.bruteforce_kda(S0, q, k, v, np.repeat(a_s[:, None], dk, 1), beta)
+    ST2, o2 = orc.bruteforce(S0, q, k, v, a_s, beta)
+    np.testing.assert_allclose(ST1, ST2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    # and the quantized per-channel step with equal channels equals the scalar step
+    for bits in (4, 6, 8, 16):
+        tq, rq, cq, codes, s = _quant_tile(orc, rng, bits, dk, dv) if bits <= 8 else (
+            orc.encode_tile(16, dk, dv, rng.standard_normal((dk, dv)), r1, c1), r1, c1, None, None)
+        al = np.float32(0.8125)
+        t1, o1 = orc.step_tile_kda(bits, dk, dv, tq, rq, cq, q[0], k[0], v[0], np.full(dk, al, np.float32), beta[0])
+        t2, o2 = orc.step_tile(bits, dk, dv, tq, rq, cq, q[0], k[0], v[0], al, beta[0])
+        np.testing.assert_allclose(o1, o2, rtol=1e-6, atol=1e-7)
+        d1, d2 = orc.decode_tile(bits, dk, dv, t1, rq, cq), orc.decode_tile(bits, dk, dv, t2, rq, cq)
+        assert np.mean(d1 != d2) <= 0.01  # identical up to rounding-boundary flips
+
+
+def test_kda_decay_only_rows(orc):
+    """beta = 0: every row decays by its own channel gate."""
+    rng = np.random.default_rng(102)
+    dk, dv = 8, 8
+    S = rng.standard_normal((dk, dv))
+    tile, r1, c1 = _fp32_tile(orc, S)
+    a = _f32(rng.uniform(0.1, 1.0, dk))
+    nt, _ = orc.step_tile_kda(32, dk, dv, tile, r1, c1, np.zeros(dk), np.zeros(dk), np.zeros(dv), a, 0.0)
+    S32 = orc.decode_tile(32, dk, dv, tile, r1, c1)
+    want = (a.astype(np.float64)[:, None] * S32).astype(np.float32).astype(np.float64)
+    assert np.array_equal(orc.decode_tile(32, dk, dv, nt, r1, c1), want)
+
+
+def test_kda_pool_matches_tiles_and_threads(orc):
+    """The pool-level per-channel step equals tile-by-tile steps, for any thread count."""
+    rng = np.random.default_rng(103)
+    bits = np.array([4, 6, 8, 16, 32], np.uint8)
+    H, dk, dv, n_req = 5, 8, 12, 3
+    r = _f32(rng.uniform(0.01, 0.02, (H, dk)))
+    c = _f32(rng.uniform(0.5, 1.5, (H, dv)))
+    off, slab = orc.pool_layout(bits, dk, dv)
+    slots = np.array([2, 0, 3], np.int32)
+    pool = rng.integers(0, 256, 4 * slab).astype(np.uint8)
+    q, k = _f32(rng.standard_normal((n_req, H, dk))), _f32(rng.standard_normal((n_req, H, dk)))
+    v = _f32(rng.standard_normal((n_req, H, dv)))
+    a = _f32(rng.uniform(0.3, 1.0, (n_req, H, dk)))
+    b = _f32(rng.uniform(0, 1, (n_req, H)))
+    # random bytes are valid codes for 4/6/8 bits; give 16/32-bit heads finite values
+    S = rng.standard_normal((dk, dv))
+    for p in range(4):
+        for h in (3, 4):
+            t = orc.encode_tile(int(bits[h]), dk, dv, S, r[h], c[h])
+            pool[p * slab + off[h]:p * slab + off[h] + t.size] = t
+    want = pool.copy()
+    o_want = np.empty((n_req, H, dv), np.float32)
+    for n, p in enumerate(slots):
+        for h in range(H):
+            o0 = p * slab + off[h]
+            nb = dk * dv * int(bits[h]) // 8
+            t, o_want[n, h] = orc.step_tile_kda(int(bits[h]), dk, dv, want[o0:o0 + nb], r[h], c[h],
+                                                q[n, h], k[n, h], v[n, h], a[n, h], b[n, h])
+            want[o0:o0 + nb] = t
+    for threads in (1, 4):
+        got = pool.copy()
+        o = orc.step_pool_kda(got, bits, dk, dv, r, c, slots, q, k, v, a, b, n_threads=threads)
+        assert np.array_equal(got, want)
+        assert np.array_equal(o, o_want)
