@@ -50,7 +50,12 @@ def algorithmic_bytes_per_step(w, bits) -> int:
     return state + io
 
 
-def traffic_from_profile(sha: str):
+# rocprofv3 kernel names of the two timed step instances (bf16 q/k/v)
+STEP_KERNEL = "k_step128<unsigned short, true, false, 128, 5>"
+KDA_KERNEL = "k_step128<unsigned short, true, true, 128, 5>"
+
+
+def traffic_from_profile(sha: str, which: str = "step"):
     """HBM bytes per launch measured by rocprofv3 counters for this exact kernel
     source, scaled by the copy-kernel calibration; None if absent or stale."""
     try:
@@ -58,9 +63,9 @@ def traffic_from_profile(sha: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != sha:
+    if t.get("kernel_source_sha") != sha or which not in t:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t[which].get("hbm_bytes_per_launch")
 
 
 COPY_BYTES = 1 << 30  # the calibration copy of --copy-calibration
@@ -69,10 +74,11 @@ COPY_BYTES = 1 << 30  # the calibration copy of --copy-calibration
 def _pmc_rows(path, counter):
     import csv
     rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-    step = [float(r["Counter_Value"]) * 1024 for r in rows if "k_step128" in r["Kernel_Name"]]
+    step = [float(r["Counter_Value"]) * 1024 for r in rows if STEP_KERNEL in r["Kernel_Name"]]
+    kda = [float(r["Counter_Value"]) * 1024 for r in rows if KDA_KERNEL in r["Kernel_Name"]]
     copies = [float(r["Counter_Value"]) * 1024 for r in rows
               if "copyBuffer" in r["Kernel_Name"] or "copy_kernel" in r["Kernel_Name"]]
-    return step, copies
+    return step, kda, copies
 
 
 def pmc_summary(fetch_csv: str, write_csv: str) -> int:
@@ -80,21 +86,28 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> int:
     each scaled by the factor that makes the same counter read the known size
     of the 1 GiB calibration copy."""
     import statistics
-    fs, fc = _pmc_rows(fetch_csv, "FETCH_SIZE")
-    ws, wc = _pmc_rows(write_csv, "WRITE_SIZE")
+    fs, fk, fc = _pmc_rows(fetch_csv, "FETCH_SIZE")
+    ws, wk, wc = _pmc_rows(write_csv, "WRITE_SIZE")
     ff = COPY_BYTES / max(fc)
     fw = COPY_BYTES / max(wc)
-    fetch = statistics.median(fs) * ff
-    write = statistics.median(ws) * fw
-    out = {"kernel_source_sha": kernel_source_sha(), "fetch_bytes_per_launch": fetch,
-           "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
-           "fetch_factor": ff, "write_factor": fw, "dispatches": [len(fs), len(ws)],
-           "raw_fetch_kib": statistics.median(fs) / 1024, "raw_write_kib": statistics.median(ws) / 1024,
+
+    def one(kernel, f, w):
+        fetch = statistics.median(f) * ff
+        write = statistics.median(w) * fw
+        return {"kernel": kernel, "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+                "hbm_bytes_per_launch": fetch + write, "dispatches": [len(f), len(w)],
+                "raw_fetch_kib": statistics.median(f) / 1024,
+                "raw_write_kib": statistics.median(w) / 1024}
+
+    out = {"kernel_source_sha": kernel_source_sha(), "step": one(STEP_KERNEL, fs, ws),
+           "fetch_factor": ff, "write_factor": fw,
            "calibration": "1 GiB device copy (hipMemcpy D2D blit kernel): FETCH_SIZE and WRITE_SIZE "
                           "each scaled so that it reads 1 GiB",
            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o <name> -- python3 "
-                        f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration"
-                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+                        f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp32-baseline "
+                        f"--copy-calibration" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    if fk and wk:
+        out["channel_gate_step"] = one(KDA_KERNEL, fk, wk)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -105,7 +118,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> int:
 def trace_summary(stats_csv: str) -> int:
     import csv
     for r in csv.DictReader(open(stats_csv)):
-        if "k_step128" in r["Name"]:
+        if "k_step128" in r["Name"] and "_f32" not in r["Name"]:
             print(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} |")
     return 0
@@ -183,6 +196,7 @@ def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, 
     byts = algorithmic_bytes_per_step(w, bits) + w.n_req * w.n_heads * 4 * (w.dk - 1)
     gbps = byts / (ms / 1e3) / 1e9
     return {"value": w.n_req * w.n_heads / (ms / 1e3), "unit": "heads*tokens/s",
+            "traffic": traffic_from_profile(kernel_source_sha(), "channel_gate_step"),
             "ms_per_step": ms, "hbm_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": byts, "time_vs_scalar_gate_step": ms / quant_ms,
             "kernel": "k_step128 per-channel-gate instance"}
