@@ -273,6 +273,7 @@ struct Smem128 {
     alignas(16) float4 wg[128];    // per-row {w 2^-s0, w 2^-s1, g 2^-s0, g 2^-s1} (half codes)
     alignas(16) float red[8][2][128];  // [row group][u, y][column] partial sums
     alignas(16) float b[128];      // per-column (v_j - alpha u_j) / c_j
+    alignas(8) float2 vc[128];     // per-column {v_j, c_j}, staged at the start
     float sum[2][3];               // per-wave partials of q.k, sum w, sum g
 };
 
@@ -520,34 +521,37 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
     const T *k = reinterpret_cast<const T *>(a.k);
     const T *v = reinterpret_cast<const T *>(a.v);
 
+    // the per-row (q, k, r, gate) and per-column (v, c) inputs of thread t
+    // are loaded before the tile: vector loads complete in issue order, so
+    // the row factors can be formed while the tile is still in flight
+    const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
+    const float beta = UPDATE ? a.beta[nh] : 0.0f;
+    // (one row and one column per thread: the row stage below assumes TPB = 128)
+    static_assert(TPB == 128, "one row and one column per thread");
+    const float qi = ld1(q, nh * 128 + t);
+    const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
+    const float rs = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
+    const float gate = CHG ? a.alpha[nh * 128 + t] : 1.0f;
+    const float vj = UPDATE ? ld1(v, nh * 128 + t) : 0.0f;
+    const float cjs = QUANT ? a.csc[(long)h * 128 + t] : 1.0f;
+
     // block (rg + RG m, cb) of the tile; the 64 lanes of a wave cover 64
     // consecutive blocks for every m (global loads measured faster on gfx950
     // than buffer loads with a per-tile resource)
-    uint32_t hv[MB][8];
-    {
-        uint32_t d[MB][W];
+    uint32_t d[MB][W];
 #pragma unroll
-        for (int m = 0; m < MB; m++)
-            load_block<BITS, NT>(tile + (long)((rg + RG * m) * 32 + cb) * BLK_BYTES, d[m]);
-#pragma unroll
-        for (int m = 0; m < MB; m++) to_halves<BITS>(d[m], hv[m]);
-    }
+    for (int m = 0; m < MB; m++)
+        load_block<BITS, NT>(tile + (long)((rg + RG * m) * 32 + cb) * BLK_BYTES, d[m]);
 
     // per-channel gate: alpha_i scales row i of the weights, the column terms
     // take alpha = 1 (u = (diag(alpha) S)^T k, o = y + beta (q.k) (v - u))
-    const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
-    const float beta = UPDATE ? a.beta[nh] : 0.0f;
-
-    if (t < 128) {
-        const float qi = ld1(q, nh * 128 + t);
-        const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
-        const float ri = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
-        const float gate = CHG ? a.alpha[nh * 128 + t] : 1.0f;
-        const float wi = ki * ri * gate, gi = qi * ri * gate;
+    {
+        const float wi = ki * rs * gate, gi = qi * rs * gate;
         sm.wg[t] = make_float4(wi * SC0, wi * SC1, gi * SC0, gi * SC1);
-        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
+        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(rs) : beta * ki;
         if constexpr (CHG) sm.pa[t] = make_float4(ai, gate * SC0, gate * SC1, OFF * (1.0f - gate));
         else if (UPDATE) sm.a[t] = ai;
+        sm.vc[t] = make_float2(vj, cjs);
         const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
         if ((t & 63) == 0) {
             sm.sum[t >> 6][0] = s0;
@@ -556,6 +560,10 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
         }
     }
     __syncthreads();
+
+    uint32_t hv[MB][8];
+#pragma unroll
+    for (int m = 0; m < MB; m++) to_halves<BITS>(d[m], hv[m]);
 
     // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
     float pu[4] = {0, 0, 0, 0}, py[4] = {0, 0, 0, 0};
@@ -591,15 +599,16 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
         const float qk = sm.sum[0][0] + sm.sum[1][0];
         const float Wsum = sm.sum[0][1] + sm.sum[1][1];
         const float Gsum = sm.sum[0][2] + sm.sum[1][2];
-        const float cjs = QUANT ? a.csc[(long)h * 128 + t] : 1.0f;
-        const float uj = cjs * (U - OFF * Wsum);
-        const float yj = cjs * (Y - OFF * Gsum);
+        const float2 vc = sm.vc[t];
+        const float cj = vc.y;
+        const float uj = cj * (U - OFF * Wsum);
+        const float yj = cj * (Y - OFF * Gsum);
         if (!UPDATE) {
             a.o[nh * 128 + t] = yj;
         } else {
-            const float e = ld1(v, nh * 128 + t) - alpha * uj;
+            const float e = vc.x - alpha * uj;
             if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * qk * e);
-            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cjs) : e;
+            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cj) : e;
         }
     }
     if (!UPDATE) return;
