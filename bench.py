@@ -105,7 +105,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> int:
                           "each scaled so that it reads 1 GiB",
            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o <name> -- python3 "
                         f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp32-baseline "
-                        f"--copy-calibration" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+                        f"--no-copy-ceiling --copy-calibration" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
     if fk and wk:
         out["channel_gate_step"] = one(KDA_KERNEL, fk, wk)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -202,6 +202,42 @@ def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, 
             "kernel": "k_step128 per-channel-gate instance"}
 
 
+def copy_ceiling(dev, stream, nbytes=2 << 30, reps=10):
+    """Device-to-device copy rate measured in the same process (torch copy_,
+    i.e. the runtime's blit kernel): bytes read + written per second.  A
+    practical bandwidth ceiling for a read-and-write stream, next to the
+    nominal peak."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": 2 * nbytes / (ms / 1e3) / 1e9, "bytes_per_copy": nbytes, "ms_per_copy": ms,
+            "what": "device-to-device copy (torch copy_), read + write bytes per second"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
     """The oracle, as it stands, on a bounded sample: whole requests (all 2304
     heads) of the same workload, calibrated to about target_s seconds."""
@@ -227,7 +263,7 @@ def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
     n = max(1, min(w.n_req, int(target_s / max(t1, 1e-3))))
     tn = run(n) if n > 1 else t1
     return {"value": n * w.n_heads / tn, "unit": "heads*tokens/s", "cores": n_threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n} of {w.n_req} requests x all {w.n_heads} heads, one decode step "
                       f"({n * w.n_heads} tiles, {tn:.1f} s wall on {n_threads} threads)"}
 
@@ -246,6 +282,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-baseline", action="store_true",
                     help="skip timing the unquantized FP32-state step at the same shape")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip timing a device-to-device copy as a practical bandwidth ceiling")
     ap.add_argument("--no-kda", action="store_true",
                     help="skip timing the per-key-channel-gate step at the same shape")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -380,6 +418,13 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+
+    if not args.no_copy_ceiling:
+        cc = copy_ceiling(dev, stream)
+        result["roofline"]["copy_ceiling_gbps"] = cc["gbps"]
+        result["roofline"]["frac_of_copy_ceiling"] = gbps / cc["gbps"]
+        result["copy_ceiling"] = cc
+        log(f"[bench] D2D copy ceiling: {cc['gbps']:.0f} GB/s; step at {gbps / cc['gbps']:.3f} of it")
 
     if not args.no_kda:
         result["channel_gate_step"] = channel_gate_step(sq, I, w, bits, pool, slots, dev, stream,

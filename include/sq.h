@@ -52,8 +52,8 @@
  *     visible after the caller synchronizes that stream.  Calls that touch the
  *     same pool must be ordered on one stream.
  *   - A slot must not appear twice in one slot_ids batch: two workgroups would
- *     update the same tile (undefined result).  Slot ids are not checked on
- *     the device.
+ *     update the same tile (undefined result).  The step does not check slot
+ *     ids on the device; sq_check_slots does, as a separate call.
  *   - Non-finite inputs (alpha, beta, q, k, v, scales) are a caller error; the
  *     resulting codes are unspecified but stay in the code range.
  *   - d_k and d_v must be multiples of 4 and at most 256; d_k = d_v = 128 takes
@@ -170,6 +170,20 @@ int sq_decode_step_kda(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, co
  * is a no-op.  Asynchronous on `stream`. */
 int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
                int32_t q_dtype, float *o, void *stream);
+
+/* Device-side check of a batch's slot ids, for callers that cannot vouch for
+ * them (the step does not check them; a repeated id makes two workgroups
+ * update one tile).  Each request owns one resident state ([P1] 背景, [P5]
+ * opening), so a valid batch names distinct slots in [0, n_slots).
+ * Writes to *result (DEVICE int32, 4-byte aligned) 0 if the batch is valid,
+ * otherwise a bit set: 1 = some id outside [0, n_slots), 2 = some id repeated.
+ * slot_ids: DEVICE int32 [n_req]; n_req == 0 writes 0.  Uses per-slot stamps
+ * in the pool's device table; calls on one pool must be stream-ordered.
+ * Errors: SQ_ERR_INVALID (null pool/result, negative n_req, misaligned
+ * result), SQ_ERR_HIP.  Asynchronous on `stream`: read *result after
+ * synchronizing it. */
+int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_t *result,
+                   void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *sq_status_string(int status);

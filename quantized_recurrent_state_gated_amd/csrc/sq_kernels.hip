@@ -979,4 +979,46 @@ hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_r
     return launch_t<float>(op, bits, a, n_req, stream);
 }
 
+// ---------------------------------------------------------------- slot check
+//
+// Batch validation, separate from the step: every id in [0, n_slots) and no
+// id twice.  Each pool keeps an int32 stamp per slot; a call with generation
+// g exchanges g into the stamp of every id it sees, and an id whose old stamp
+// is already g has been seen earlier in the same call.  Flags: 1 = an id out
+// of range, 2 = an id repeated.
+
+__global__ __launch_bounds__(64) void k_flag_clear(int32_t *flag, int32_t *stamps, int32_t n_slots)
+{
+    // stamps != nullptr: also reset every stamp (generation wrap-around)
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    if (i == 0) flag[0] = 0;
+    if (stamps)
+        for (int s = i; s < n_slots; s += gridDim.x * 64) stamps[s] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_check_slots(const int32_t *ids, int32_t n, int32_t n_slots,
+                                                     int32_t *stamps, int32_t gen, int32_t *flag)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int32_t id = ids[i];
+    if (id < 0 || id >= n_slots) {
+        atomicOr(flag, 1);
+        return;
+    }
+    if (atomicExch(stamps + id, gen) == gen) atomicOr(flag, 2);
+}
+
+hipError_t launch_check_slots(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *stamps,
+                              int32_t gen, bool reset_stamps, int32_t *flag, hipStream_t st)
+{
+    const unsigned clear_blocks = reset_stamps ? (unsigned)((n_slots + 63) / 64) : 1u;
+    hipLaunchKernelGGL(k_flag_clear, dim3(clear_blocks > 4096 ? 4096 : clear_blocks), dim3(64), 0,
+                       st, flag, reset_stamps ? stamps : nullptr, n_slots);
+    if (n > 0)
+        hipLaunchKernelGGL(k_check_slots, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids,
+                           n, n_slots, stamps, gen, flag);
+    return hipGetLastError();
+}
+
 }  // namespace sqk

@@ -26,7 +26,7 @@ SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM = 0, -1, -2,
 SQ_F32, SQ_BF16 = 0, 1
 EXPORTED = ("sq_pool_bytes", "sq_pool_alloc", "sq_pool_free", "sq_pool_tile_offset",
             "sq_pool_store", "sq_pool_load", "sq_decode_step", "sq_decode_step_kda", "sq_readout",
-            "sq_status_string")
+            "sq_check_slots", "sq_status_string")
 
 
 class SqPoolDesc(ctypes.Structure):
@@ -57,6 +57,8 @@ _lib.sq_decode_step_kda.restype = ctypes.c_int
 _lib.sq_decode_step_kda.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
 _lib.sq_readout.restype = ctypes.c_int
 _lib.sq_readout.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp]
+_lib.sq_check_slots.restype = ctypes.c_int
+_lib.sq_check_slots.argtypes = [_vp, _vp, _i32, _vp, _vp]
 _lib.sq_status_string.restype = ctypes.c_char_p
 _lib.sq_status_string.argtypes = [ctypes.c_int]
 
@@ -99,6 +101,14 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _bits_array(head_bits):
     hb = bytes(int(b) for b in head_bits)
     return (ctypes.c_uint8 * max(len(hb), 1)).from_buffer_copy(hb or b"\0"), len(hb)
+
+
+def sq_check_slots(pool: SqPool, slot_ids, result, stream=None) -> None:
+    """Write into the int32 device tensor `result` 0 for a valid batch, else
+    1 (id out of range) | 2 (id repeated)."""
+    n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    _check(_lib.sq_check_slots(pool.handle, _ptr(slot_ids), n_req, _ptr(result), _stream(stream)),
+           "sq_check_slots")
 
 
 def sq_status_string(status: int) -> str:

@@ -80,6 +80,7 @@ def test_null_handles_and_status_strings(sq):
     assert sq._lib.sq_decode_step_kda(None, None, 1, None, None, None, 0, None, None, None,
                                       None) == -1
     assert sq._lib.sq_readout(None, None, 1, None, 0, None, None) == -1
+    assert sq._lib.sq_check_slots(None, None, 0, None, None) == -1
     assert sq._lib.sq_pool_store(None, None, 1, None, None) == -1
     off = ctypes.c_uint64()
     assert sq._lib.sq_pool_tile_offset(None, 0, 0, ctypes.byref(off), ctypes.byref(off)) == -1

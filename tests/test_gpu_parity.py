@@ -230,3 +230,33 @@ def test_host_errors_with_a_live_pool(sq, orc):
     assert off == case.slab + int(case.off[3]) and nb == orc.tile_bytes(int(case.bits[3]), 128, 128)
     with pytest.raises(sq.SqError):
         sq.sq_pool_tile_offset(case.pool, 2, 0)
+
+
+def test_check_slots(sq, orc):
+    """sq_check_slots flags ids out of range (1) and repeated ids (2), and
+    successive calls on one pool stay independent (generation stamps)."""
+    w = I.scaled(I.WORKLOADS["layer"], 2, 6, 1)
+    case = Case(sq, orc, w, n_slots=9, slots=[3, 5])
+    res = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+
+    def check(ids):
+        t = torch.tensor(ids, dtype=torch.int32, device="cuda")
+        sq.sq_check_slots(case.pool, t, res)
+        torch.cuda.synchronize()
+        return int(res.item())
+
+    assert check([3, 5]) == 0
+    assert check([0, 1, 2, 3, 4, 5, 6, 7, 8]) == 0
+    assert check([8, 0, 8]) == 2
+    assert check([3, 5]) == 0  # stamps from the previous calls do not leak
+    assert check([9]) == 1 and check([-1, 2]) == 1
+    assert check([4, 9, 4]) == 3
+    assert check(list(range(9))[::-1]) == 0
+    assert check([]) == 0
+    big = torch.arange(9, dtype=torch.int32, device="cuda").repeat(300)  # 2700 ids, many blocks
+    sq.sq_check_slots(case.pool, big, res)
+    torch.cuda.synchronize()
+    assert int(res.item()) == 2
+    pre = case.host()
+    assert check([0, 1]) == 0
+    assert np.array_equal(case.host(), pre)  # the check never touches the pool
