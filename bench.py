@@ -105,7 +105,8 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> int:
                           "each scaled so that it reads 1 GiB",
            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o <name> -- python3 "
                         f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp32-baseline "
-                        f"--no-copy-ceiling --copy-calibration" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+                        f"--no-copy-ceiling --copy-calibration"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
     if fk and wk:
         out["channel_gate_step"] = one(KDA_KERNEL, fk, wk)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -202,6 +203,52 @@ def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, 
             "kernel": "k_step128 per-channel-gate instance"}
 
 
+def small_batch_graph(sq, I, dev, steps=16, reps=20):
+    """The layer workload (8 requests x 48 heads, 384 tiles: cache-resident and
+    launch-bound) stepped eagerly and as a HIP graph of `steps` captured
+    steps; per-step times of both.  Context for the small-batch regime."""
+    import torch
+
+    w = I.WORKLOADS["layer"]
+    bits = I.head_bits(w)
+    r, c = I.scales(w, device=dev)
+    nbytes = sq.sq_pool_bytes(w.n_req, w.n_heads, w.dk, w.dv, bits)
+    state = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pool = sq.sq_pool_alloc(w.n_req, w.n_heads, w.dk, w.dv, bits, r, c, state)
+    slots = torch.arange(w.n_req, dtype=torch.int32, device=dev)
+    for p in range(w.n_req):
+        sq.sq_pool_store(pool, slots[p:p + 1], I.initial_state(w, p, dev))
+    ins = [I.step_inputs(w, t, dev) for t in range(steps)]
+    o = torch.empty(w.n_req, w.n_heads, w.dv, device=dev)
+
+    def run():
+        for x in ins:
+            sq.sq_decode_step(pool, slots, x.q, x.k, x.v, x.alpha, x.beta, o)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * steps)
+
+    eager = timed(run)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    graph = timed(g.replay)
+    del g, pool, state
+    torch.cuda.empty_cache()
+    return {"workload": f"layer: {w.n_req} requests x {w.n_heads} heads ({w.tiles} tiles)",
+            "eager_ms_per_step": eager, "graph_ms_per_step": graph,
+            "steps_per_graph": steps, "speedup": eager / graph}
+
+
 def copy_ceiling(dev, stream, nbytes=2 << 30, reps=10):
     """Device-to-device copy rate measured in the same process (torch copy_,
     i.e. the runtime's blit kernel): bytes read + written per second.  A
@@ -284,6 +331,9 @@ def main() -> int:
                     help="skip timing the unquantized FP32-state step at the same shape")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip timing a device-to-device copy as a practical bandwidth ceiling")
+    ap.add_argument("--small-batch", action="store_true",
+                    help="also time the small layer workload eagerly and as a HIP graph (it runs "
+                         "the same kernel, so it is off by default to keep kernel traces clean)")
     ap.add_argument("--no-kda", action="store_true",
                     help="skip timing the per-key-channel-gate step at the same shape")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -425,6 +475,11 @@ def main() -> int:
         result["roofline"]["frac_of_copy_ceiling"] = gbps / cc["gbps"]
         result["copy_ceiling"] = cc
         log(f"[bench] D2D copy ceiling: {cc['gbps']:.0f} GB/s; step at {gbps / cc['gbps']:.3f} of it")
+
+    if args.small_batch:
+        result["small_batch_graph"] = small_batch_graph(sq, I, dev)
+        log(f"[bench] layer workload: {result['small_batch_graph']['eager_ms_per_step'] * 1e3:.1f} us "
+            f"eager, {result['small_batch_graph']['graph_ms_per_step'] * 1e3:.1f} us in a graph")
 
     if not args.no_kda:
         result["channel_gate_step"] = channel_gate_step(sq, I, w, bits, pool, slots, dev, stream,

@@ -178,7 +178,9 @@ int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, cons
  * Writes to *result (DEVICE int32, 4-byte aligned) 0 if the batch is valid,
  * otherwise a bit set: 1 = some id outside [0, n_slots), 2 = some id repeated.
  * slot_ids: DEVICE int32 [n_req]; n_req == 0 writes 0.  Uses per-slot stamps
- * in the pool's device table; calls on one pool must be stream-ordered.
+ * and a generation counter in the pool's device table (no host state), so the
+ * call can be captured in a HIP graph and replayed; calls on one pool must be
+ * stream-ordered.
  * Errors: SQ_ERR_INVALID (null pool/result, negative n_req, misaligned
  * result), SQ_ERR_HIP.  Asynchronous on `stream`: read *result after
  * synchronizing it. */

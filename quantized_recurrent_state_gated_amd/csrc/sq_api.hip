@@ -71,11 +71,10 @@ struct sq_pool {
     uint64_t state_bytes;
     int device;
     void *dtab;               // device: int64 head_off[H] | int32 heads grouped by class | u8 bits[H]
-                              //         | pad to 4 | int32 slot stamps[n_slots]
+                              //         | pad to 4 | int32 slot stamps[n_slots] | int32 generation
     int64_t *d_off;
     uint8_t *d_bits;
-    int32_t *d_stamps;        // sq_check_slots' per-slot generation stamps, zeroed at alloc
-    int32_t check_gen;        // generation of the last sq_check_slots call
+    int32_t *d_stamps;        // sq_check_slots' per-slot stamps + generation, zeroed at alloc
     int32_t *d_heads[5];
     int32_t n_class[5];
 };
@@ -123,7 +122,7 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     // host image of the device table: offsets, then head ids grouped by width
     const size_t H = (size_t)d.n_heads;
     const size_t stamps_at = (H * 13 + 3) / 4 * 4;
-    std::vector<unsigned char> img(stamps_at + (size_t)d.n_slots * 4, 0);
+    std::vector<unsigned char> img(stamps_at + ((size_t)d.n_slots + 1) * 4, 0);
     memcpy(img.data(), off.data(), H * 8);
     int32_t *heads = reinterpret_cast<int32_t *>(img.data() + H * 8);
     size_t pos = 0;
@@ -156,7 +155,6 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     for (int c = 0; c < 5; c++) p->d_heads[c] = dheads + start[c];
     p->d_bits = static_cast<unsigned char *>(p->dtab) + H * 12;
     p->d_stamps = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(p->dtab) + stamps_at);
-    p->check_gen = 0;
     *out = p;
     return SQ_OK;
 }
@@ -315,14 +313,8 @@ int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_
 {
     if (!pool || !result || n_req < 0 || (n_req > 0 && !slot_ids) || !aligned(result, 4))
         return SQ_ERR_INVALID;
-    bool reset = false;
-    if (pool->check_gen == 0x7fffffff) {  // wrap: stale stamps could equal a new generation
-        pool->check_gen = 0;
-        reset = true;
-    }
-    pool->check_gen++;
-    if (sqk::launch_check_slots(slot_ids, n_req, pool->n_slots, pool->d_stamps, pool->check_gen,
-                                reset, result, (hipStream_t)stream) != hipSuccess)
+    if (sqk::launch_check_slots(slot_ids, n_req, pool->n_slots, pool->d_stamps, result,
+                                (hipStream_t)stream) != hipSuccess)
         return SQ_ERR_HIP;
     return SQ_OK;
 }

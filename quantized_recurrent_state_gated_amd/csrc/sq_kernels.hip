@@ -982,22 +982,36 @@ hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_r
 // ---------------------------------------------------------------- slot check
 //
 // Batch validation, separate from the step: every id in [0, n_slots) and no
-// id twice.  Each pool keeps an int32 stamp per slot; a call with generation
-// g exchanges g into the stamp of every id it sees, and an id whose old stamp
-// is already g has been seen earlier in the same call.  Flags: 1 = an id out
-// of range, 2 = an id repeated.
+// id twice.  Each pool keeps an int32 stamp per slot and, after them, the
+// generation of the last check.  A check first advances the generation g
+// (one thread, which also clears the flag), then exchanges g into the stamp
+// of every id it sees; an id whose old stamp is already g has been seen
+// earlier in the same check.  The generation lives in device memory, so a
+// captured graph of the two launches stays correct on every replay.  Flags:
+// 1 = an id out of range, 2 = an id repeated.
 
-__global__ __launch_bounds__(64) void k_flag_clear(int32_t *flag, int32_t *stamps, int32_t n_slots)
+constexpr int32_t kGenMax = 0x7fffffff;
+
+__global__ __launch_bounds__(256) void k_check_begin(int32_t *flag, int32_t *stamps, int32_t n_slots)
 {
-    // stamps != nullptr: also reset every stamp (generation wrap-around)
-    const int i = blockIdx.x * 64 + threadIdx.x;
-    if (i == 0) flag[0] = 0;
-    if (stamps)
-        for (int s = i; s < n_slots; s += gridDim.x * 64) stamps[s] = 0;
+    // stamps[n_slots] is the generation; when it would wrap, every stamp is
+    // zeroed first so that no stale stamp can equal a new generation
+    __shared__ int32_t wrap;
+    int32_t *gen = stamps + n_slots;
+    if (threadIdx.x == 0) wrap = gen[0] >= kGenMax;
+    __syncthreads();
+    if (wrap) {
+        for (int32_t s = threadIdx.x; s < n_slots; s += 256) stamps[s] = 0;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        gen[0] = wrap ? 1 : gen[0] + 1;
+        flag[0] = 0;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_check_slots(const int32_t *ids, int32_t n, int32_t n_slots,
-                                                     int32_t *stamps, int32_t gen, int32_t *flag)
+                                                     int32_t *stamps, int32_t *flag)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
@@ -1006,18 +1020,17 @@ __global__ __launch_bounds__(256) void k_check_slots(const int32_t *ids, int32_t
         atomicOr(flag, 1);
         return;
     }
+    const int32_t gen = stamps[n_slots];
     if (atomicExch(stamps + id, gen) == gen) atomicOr(flag, 2);
 }
 
 hipError_t launch_check_slots(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *stamps,
-                              int32_t gen, bool reset_stamps, int32_t *flag, hipStream_t st)
+                              int32_t *flag, hipStream_t st)
 {
-    const unsigned clear_blocks = reset_stamps ? (unsigned)((n_slots + 63) / 64) : 1u;
-    hipLaunchKernelGGL(k_flag_clear, dim3(clear_blocks > 4096 ? 4096 : clear_blocks), dim3(64), 0,
-                       st, flag, reset_stamps ? stamps : nullptr, n_slots);
+    hipLaunchKernelGGL(k_check_begin, dim3(1), dim3(256), 0, st, flag, stamps, n_slots);
     if (n > 0)
         hipLaunchKernelGGL(k_check_slots, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids,
-                           n, n_slots, stamps, gen, flag);
+                           n, n_slots, stamps, flag);
     return hipGetLastError();
 }
 

@@ -50,10 +50,10 @@ hipError_t launch_f32_128(Op op, bool qkv_bf16, const StepArgs &a, int32_t n_req
 hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,
                           hipStream_t stream);
 
-// Clear *flag, then flag slot ids out of [0, n_slots) (bit 0) or repeated
-// (bit 1) using the per-slot stamps and generation gen (nonzero).
-// reset_stamps zeroes every stamp first (after a generation wrap-around).
+// Advance the check generation (stamps[n_slots]) and clear *flag, then flag
+// slot ids out of [0, n_slots) (bit 0) or repeated (bit 1).  stamps holds
+// n_slots + 1 int32, zeroed when the pool is made.
 hipError_t launch_check_slots(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *stamps,
-                              int32_t gen, bool reset_stamps, int32_t *flag, hipStream_t stream);
+                              int32_t *flag, hipStream_t stream);
 
 }  // namespace sqk
