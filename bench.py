@@ -203,6 +203,39 @@ def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, 
             "kernel": "k_step128 per-channel-gate instance"}
 
 
+def saturation(sq, w, bits, pool, state):
+    """Fraction of stored codes at the ends of the symmetric range (+-Q) per
+    width, read from the pool bytes after the timed steps: a proxy for the
+    requantizer's clamp rate (a code at +-Q was clamped or rounded onto the
+    bound).  torch integer ops on the bytes; diagnostic only."""
+    import numpy as np
+    import torch
+
+    slab = state.numel() // w.n_req
+    rows = state[: w.n_req * slab].view(w.n_req, slab)
+    out = {}
+    for b in (4, 6, 8):
+        hs = np.nonzero(bits == b)[0]
+        if hs.size == 0:
+            continue
+        offs = [sq.sq_pool_tile_offset(pool, 0, int(h)) for h in hs]
+        nb = offs[0][1]
+        idx = torch.tensor([o for o, _ in offs], device=state.device)[:, None] + \
+            torch.arange(nb, device=state.device)[None, :]
+        t = rows[:, idx].to(torch.int32)  # [n_req][heads of width b][tile bytes]
+        if b == 8:
+            f = t
+        elif b == 4:
+            f = torch.stack([t & 15, t >> 4], -1)
+        else:
+            g = t.view(w.n_req, hs.size, -1, 3)
+            word = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+            f = torch.stack([(word >> sh) & 63 for sh in (0, 6, 12, 18)], -1)
+        out[str(b)] = float(((f == 1) | (f == (1 << b) - 1)).double().mean())
+        del t, f
+    return out
+
+
 def small_batch_graph(sq, I, dev, steps=16, reps=20):
     """The layer workload (8 requests x 48 heads, 384 tiles: cache-resident and
     launch-bound) stepped eagerly and as a HIP graph of `steps` captured
@@ -468,6 +501,9 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+
+    result["saturated_code_fraction"] = saturation(sq, w, bits, pool, state)
+    log(f"[bench] codes at +-Q after the timed steps: {result['saturated_code_fraction']}")
 
     if not args.no_copy_ceiling:
         cc = copy_ceiling(dev, stream)

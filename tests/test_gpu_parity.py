@@ -260,3 +260,41 @@ def test_check_slots(sq, orc):
     pre = case.host()
     assert check([0, 1]) == 0
     assert np.array_equal(case.host(), pre)  # the check never touches the pool
+
+
+def test_non_finite_inputs_stay_in_range(sq, orc):
+    """A NaN or infinite gate / write strength is a caller error: the codes of
+    that tile are unspecified but stay in the symmetric range (no field at the
+    excluded code, no spill into neighbouring fields), and every other tile
+    matches the oracle."""
+    w = I.Workload("nonfinite", 3, 10, 128, 128, 1, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, seed=31)
+    case = Case(sq, orc, w)
+    pre = case.host()
+    si = I.step_inputs(w, 0)
+    bad = [(0, h) for h in range(w.n_heads)] + [(1, 2), (1, 5)]
+    for n, h in bad:
+        si.alpha[n, h] = float("nan") if (n + h) % 2 == 0 else float("inf")
+    si.beta[1, 2] = float("nan")
+    o = case.step(si)
+    post = case.host()
+    H = w.n_heads
+    for n, p in enumerate(case.slots):
+        for h in range(H):
+            b = int(case.bits[h])
+            if b > 8:
+                continue
+            tb = orc.tile_bytes(b, w.dk, w.dv)
+            lo = int(p) * case.slab + int(case.off[h])
+            f = unpack_fields(post[None, lo:lo + tb], b)
+            assert f.min() >= 1 and f.max() <= 2 ** b - 1, (n, h, b)
+    # the finite tiles: teacher-forced oracle comparison on the requests and heads not touched
+    ref, o_ref = case.oracle_step(pre, si)
+    tally = Tally()
+    good = [(n, h) for n in range(w.n_req) for h in range(H) if (n, h) not in bad]
+    for n, h in good:
+        b = int(case.bits[h])
+        tb = orc.tile_bytes(b, w.dk, w.dv)
+        lo = int(case.slots[n]) * case.slab + int(case.off[h])
+        tally.add_tiles(post[None, lo:lo + tb], ref[None, lo:lo + tb], b)
+        tally.add_o(o[n, h].cpu().numpy()[None], o_ref[n, h][None])
+    tally.check()
