@@ -303,30 +303,39 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
     const T *k = reinterpret_cast<const T *>(a.k);
     const T *v = reinterpret_cast<const T *>(a.v);
 
-    // the tile: 4 blocks per thread, issued first
-    uint32_t d[4][W];
-#pragma unroll
-    for (int m = 0; m < 4; m++) load_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
-
     // with a per-channel gate alpha_i multiplies row i of the weights and the
     // column terms take alpha = 1: u = (diag(alpha) S)^T k, o = y + beta (q.k) (v - u)
     const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
     const float beta = UPDATE ? a.beta[nh] : 0.0f;
 
-    // per-row factors (threads 0..127, one row each) and the three tile sums
-    if (t < 128) {
-        const float qi = ld1(q, nh * 128 + t);
-        const float ki = UPDATE ? ld1(k, nh * 128 + t) : 0.0f;
-        const float ri = QUANT ? a.rsc[(long)h * 128 + t] : 1.0f;
-        const float gate = CHG ? a.alpha[nh * 128 + t] : 1.0f;
-        const float wi = ki * ri * gate, gi = qi * ri * gate;
-        sm.w[t] = wi;
-        sm.g[t] = gi;
-        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(ri) : beta * ki;
-        if constexpr (CHG) sm.pa[t] = make_float4(ai, gate, gate, OFF * (1.0f - gate));
-        else if (UPDATE) sm.a[t] = ai;
+    // row tr = t % 128 inputs (threads 128..255 repeat rows 0..127) and column
+    // tr inputs, loaded before the tile: vector loads complete in issue order,
+    // so the row stage does not wait for the tile
+    const int tr = t & 127;
+    const float qi = ld1(q, nh * 128 + tr);
+    const float ki = UPDATE ? ld1(k, nh * 128 + tr) : 0.0f;
+    const float rs = QUANT ? a.rsc[(long)h * 128 + tr] : 1.0f;
+    const float gate = CHG ? a.alpha[nh * 128 + tr] : 1.0f;
+    const float vj = UPDATE ? ld1(v, nh * 128 + tr) : 0.0f;
+    const float cjs = QUANT ? a.csc[(long)h * 128 + tr] : 1.0f;
+
+    // the tile: 4 blocks per thread
+    uint32_t d[4][W];
+#pragma unroll
+    for (int m = 0; m < 4; m++) load_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
+
+    // per-row factors and the three tile sums (waves 0 and 1 hold rows 0..127;
+    // waves 2 and 3 write the same values again)
+    {
+        const float wi = ki * rs * gate, gi = qi * rs * gate;
+        sm.w[tr] = wi;
+        sm.g[tr] = gi;
+        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(rs) : beta * ki;
+        if constexpr (CHG) sm.pa[tr] = make_float4(ai, gate, gate, OFF * (1.0f - gate));
+        else if (UPDATE) sm.a[tr] = ai;
+        sm.vc[tr] = make_float2(vj, cjs);
         const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
-        if ((t & 63) == 0) {
+        if (t < 128 && (t & 63) == 0) {
             sm.sum[t >> 6][0] = s0;
             sm.sum[t >> 6][1] = s1;
             sm.sum[t >> 6][2] = s2;
@@ -367,15 +376,16 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
         const float qk = sm.sum[0][0] + sm.sum[1][0];
         const float Wsum = sm.sum[0][1] + sm.sum[1][1];
         const float Gsum = sm.sum[0][2] + sm.sum[1][2];
-        const float cjs = QUANT ? a.csc[(long)h * 128 + t] : 1.0f;
-        const float uj = cjs * (U - OFF * Wsum);
-        const float yj = cjs * (Y - OFF * Gsum);
+        const float2 vc = sm.vc[t];
+        const float cj = vc.y;
+        const float uj = cj * (U - OFF * Wsum);
+        const float yj = cj * (Y - OFF * Gsum);
         if (!UPDATE) {
             a.o[nh * 128 + t] = yj;
         } else {
-            const float e = ld1(v, nh * 128 + t) - alpha * uj;
+            const float e = vc.x - alpha * uj;
             if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * qk * e);
-            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cjs) : e;
+            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cj) : e;
         }
     }
     if (!UPDATE) return;
