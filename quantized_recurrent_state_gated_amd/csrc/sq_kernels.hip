@@ -22,6 +22,12 @@
 // so the tile is touched by two fused multiply-adds per element per pass and
 // o needs no second reduction.  Codes are carried in their stored excess form
 // n = q + 2^(b-1); the bias is folded into per-tile constants.
+//
+// The per-key-channel gate (the KDA reading, [P5] 直接量化为什么会翻车:
+// S' = (I - beta k k^T) diag(alpha) Shat + beta k v^T, alpha in R^{d_k}) is
+// the same arithmetic with alpha_i moved into the row factors: u and y use
+// weights alpha_i k_i r_i and alpha_i q_i r_i, the column terms take alpha = 1,
+// and the requantization uses alpha_i per row.  Template flag CHG.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <type_traits>
@@ -259,14 +265,17 @@ __device__ __forceinline__ float wave_sum(float x)
 
 // ---------------------------------------------------------------- d = 128 step
 //
-// One 256-thread workgroup per (request, head) tile.  Thread t owns column
+// Shared memory of one tile.  Two bodies use it: tile128 (the fused launch
+// over 4/6/8-bit and FP16 tiles, 128 threads, codes held as packed halves;
+// below) and tile128_wide (FP32-state tiles, 256 threads, fp32 registers).
+//
+// tile128_wide: one 256-thread workgroup per tile.  Thread t owns column
 // block cb = t % 32 (columns 4cb..4cb+3) and row group rg = t / 32, i.e. the
 // four 4x4 blocks in block rows rg, rg+8, rg+16, rg+24 (16 rows).  For a
 // fixed m the 64 lanes of a wave read 64 consecutive blocks, so every load
-// and store instruction of a wave covers one contiguous 512 B .. 4 KB span.
-// Partial column sums over a thread's 16 rows are combined across the 8 row
-// groups through LDS.  All width classes run in one launch: the grid is the
-// concatenation of the classes' tiles, heaviest tiles first.
+// and store instruction of a wave covers one contiguous span.  Partial column
+// sums over a thread's 16 rows are combined across the 8 row groups through
+// LDS.
 
 struct Smem128 {
     float w[128], g[128], a[128];  // per-row factors k_i r_i, q_i r_i, beta k_i / r_i
