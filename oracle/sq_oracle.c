@@ -26,6 +26,10 @@
  * Every function below is a direct transcription of a definition; there is no
  * blocking, fusion or reordering.  Bit fields are read and written one bit at
  * a time on purpose.
+ *
+ * Besides the scalar-gate step, the file holds the per-key-channel-gate step
+ * (the reading of the KDA gate named in [P5] 直接量化为什么会翻车), in the
+ * same style, with a dense brute-force recurrence of its own.
  */
 #include <math.h>
 #include <pthread.h>
