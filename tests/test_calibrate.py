@@ -99,3 +99,55 @@ def test_column_update_solves_weighted_normal_equations():
     cj = num / den
     resid = S.double() - cj[None, :, None, :] * X
     assert torch.allclose((wi * X * resid).sum(dim=(0, 2)), torch.zeros_like(cj), atol=1e-9)
+
+
+def _fp32_tile(orc, S):
+    dk, dv = S.shape
+    r, c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+    return orc.encode_tile(32, dk, dv, S, r, c), r, c
+
+
+def test_row_influence_is_the_readout_sensitivity_of_the_step(orc):
+    """Perturbing row i of the state entering a step by eps moves every
+    readout o_j of that step (the oracle's FP32-state step) by eps * w_i, and
+    row_influence is E[w_i^2]: with one request and one step, (do_j / eps)^2."""
+    w = I.Workload("infl1", 1, 3, 8, 8, 1, {8: 3}, qkv_dtype="f32", seed=9)
+    infl = C.row_influence(w, 1).double().numpy()
+    si = I.step_inputs(w, 0)
+    rng = np.random.default_rng(1)
+    eps = 2.0 ** -6
+    for h in range(3):
+        S = rng.integers(-256, 256, (8, 8)) / 256.0  # exact in fp32, and so is S + eps
+        args = (si.q[0, h].numpy(), si.k[0, h].numpy(), si.v[0, h].numpy(),
+                float(si.alpha[0, h]), float(si.beta[0, h]))
+        tile, r, c = _fp32_tile(orc, S)
+        _, o0 = orc.step_tile(32, 8, 8, tile, r, c, *args)
+        for i in range(8):
+            Sp = S.copy()
+            Sp[i] += eps
+            tile, r, c = _fp32_tile(orc, Sp)
+            _, o1 = orc.step_tile(32, 8, 8, tile, r, c, *args)
+            sens = (o1.astype(np.float64) - o0) / eps
+            assert np.allclose(sens, sens[0], rtol=1e-3, atol=1e-5)  # the same for every column
+            assert abs(sens[0] ** 2 - infl[h, i]) <= 2e-3 * max(infl[h, i], 1e-3), (h, i)
+
+
+def test_lifetime_weight_is_the_energy_an_error_keeps(orc):
+    """Under the head's average decay abar (beta = 0), an error's energy after
+    t steps is abar^(2t) of the start; summed over steps it is the lifetime
+    weight 1 / (1 - abar^2).  Checked on the oracle's FP32-state step."""
+    w = I.Workload("life", 4, 3, 4, 4, 64, {8: 3}, half_life=(2.0, 6.0), qkv_dtype="f32", seed=11)
+    L = C.lifetime_weight(w, 64).double().numpy()
+    la = torch.stack([torch.log(I.step_inputs(w, t).alpha.double()) for t in range(64)])
+    abar = torch.exp(la.mean(dim=(0, 1))).numpy()
+    rng = np.random.default_rng(4)
+    zero4 = np.zeros(4, np.float32)
+    for h in range(3):
+        E0 = rng.standard_normal((4, 4))
+        tile, r, c = _fp32_tile(orc, E0)
+        e0 = float((orc.decode_tile(32, 4, 4, tile, r, c) ** 2).sum())
+        total = e0
+        for t in range(400):
+            tile, _ = orc.step_tile(32, 4, 4, tile, r, c, zero4, zero4, zero4, float(abar[h]), 0.0)
+            total += float((orc.decode_tile(32, 4, 4, tile, r, c) ** 2).sum())
+        assert abs(total / e0 - L[h]) <= 1e-4 * L[h], (h, total / e0, L[h])

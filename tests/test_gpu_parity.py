@@ -298,3 +298,39 @@ def test_non_finite_inputs_stay_in_range(sq, orc):
         tally.add_tiles(post[None, lo:lo + tb], ref[None, lo:lo + tb], b)
         tally.add_o(o[n, h].cpu().numpy()[None], o_ref[n, h][None])
     tally.check()
+
+
+def test_two_pools_on_two_streams(sq, orc):
+    """The library keeps no global state: two pools stepped concurrently on two
+    streams, from two host threads, end bit-identical to the same steps run
+    one after the other on the default stream."""
+    import threading
+
+    w = I.scaled(I.WORKLOADS["layer"], 3, 12, 8)
+    cases = [Case(sq, orc, w), Case(sq, orc, I.scaled(w, name="other"), slots=[2, 0, 1])]
+    inits = [c.dev.clone() for c in cases]
+    ins = [[I.step_inputs(w, t + 10 * k, "cuda") for t in range(w.steps)] for k in range(2)]
+
+    def run(k, stream):
+        c = cases[k]
+        with torch.cuda.stream(stream):
+            for si in ins[k]:
+                sq.sq_decode_step(c.pool, c.slots_d, si.q, si.k, si.v, si.alpha, si.beta, None,
+                                  stream)
+
+    for k in range(2):
+        run(k, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = [c.dev.clone() for c in cases]
+    for c, i0 in zip(cases, inits):
+        c.dev.copy_(i0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    th = [threading.Thread(target=run, args=(k, streams[k])) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    for c, wnt in zip(cases, want):
+        assert torch.equal(c.dev, wnt)
