@@ -48,6 +48,10 @@ def _load():
         "orc_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
         "orc_f32_to_f16_array": (None, [_f32p, _u16p, ctypes.c_long]),
         "orc_f16_to_f32_array": (None, [_u16p, _f32p, ctypes.c_long]),
+        "orc_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "orc_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_f32_to_bf16_array": (None, [_f32p, _u16p, ctypes.c_long]),
+        "orc_bf16_to_f32_array": (None, [_u16p, _f32p, ctypes.c_long]),
         "orc_elem_index": (ctypes.c_long, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "orc_field_width": (ctypes.c_int, [ctypes.c_int]),
         "orc_tile_bytes": (ctypes.c_long, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
@@ -112,6 +116,23 @@ def f16_bits_to_f32(h) -> np.ndarray:
     h = _c(h, np.uint16)
     out = np.empty(h.shape, np.float32)
     _load().orc_f16_to_f32_array(_p(h, _u16p), _p(out, _f32p), h.size)
+    return out
+
+
+BITS_BF16 = 144  # head_bits value of a bfloat16 state (16-bit fields)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_f32_to_bf16_array(_p(x, _f32p), _p(out, _u16p), x.size)
+    return out
+
+
+def bf16_bits_to_f32(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _load().orc_bf16_to_f32_array(_p(h, _u16p), _p(out, _f32p), h.size)
     return out
 
 

@@ -94,6 +94,55 @@ uint16_t orc_f32_to_f16(float x)
 }
 
 /* ------------------------------------------------------------------------ */
+/* bfloat16 <-> binary32.  A bfloat16 is the upper half of a binary32 (sign, */
+/* 8 exponent bits, 7 mantissa bits).  Used by the BF16-state format, an     */
+/* unquantized 16-bit baseline beside the FP32 state (not a format of the    */
+/* pages: a comparison point, as the FP32 state is [P1] 實驗結果).           */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_BITS_BF16 144 /* head_bits value of a bfloat16 state */
+
+float orc_bf16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int m = h & 0x7f;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)m, -133); /* zero or subnormal: m * 2^-126 * 2^-7 */
+    } else if (e == 255) {
+        if (m != 0) return nanf("");
+        v = INFINITY;
+    } else {
+        v = ldexp((double)(128 + m), e - 134); /* (1.m) * 2^(e-127) */
+    }
+    return (float)(sign ? -v : v);
+}
+
+uint16_t orc_f32_to_bf16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return (uint16_t)(sign | 0x7fc0);
+    double a = fabs((double)x);
+    if (isinf(x)) return (uint16_t)(sign | 0x7f80);
+    /* largest finite bfloat16 is (2 - 2^-7) 2^127; half an ulp above it RNE
+     * goes to infinity */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return (uint16_t)(sign | 0x7f80);
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: quantum 2^-133; n == 128 is the smallest normal */
+        double n = rne_nonneg(a / ldexp(1.0, -133));
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int E;
+    frexp(a, &E);
+    int ex = E - 1;
+    double ulp = ldexp(1.0, ex - 7);
+    double n = rne_nonneg(a / ulp); /* in [128, 256] */
+    uint32_t bits = ((uint32_t)(ex + 127) << 7) + (uint32_t)n - 128u;
+    return (uint16_t)(sign | bits);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Tile layout.                                                              */
 /*                                                                            */
 /* A tile is one head's d_k x d_v state for one request slot; rows i are key */
@@ -105,7 +154,8 @@ uint16_t orc_f32_to_f16(float x)
 /*     n = 16*B + 4*(j%4) + (i%4).                                           */
 /* Field n occupies bits [n*w, n*w + w) of the tile read as a little-endian  */
 /* bit stream, w being the field width: 4, 6 or 8 for codes, 16 for an FP16 */
-/* pivot, 32 for an FP32 state.  So 4-bit codes sit two per byte (even n in  */
+/* pivot or a bfloat16 state, 32 for an FP32 state.  So 4-bit codes sit two */
+/* per byte (even n in                                                        */
 /* the low nibble) and 6-bit codes four per three bytes (a 24-bit little-    */
 /* endian group holds fields 4g..4g+3 at bit offsets 0, 6, 12, 18).          */
 /* ------------------------------------------------------------------------ */
@@ -119,6 +169,7 @@ long orc_elem_index(int i, int j, int dv)
 int orc_field_width(int bits)
 {
     if (bits == 4 || bits == 6 || bits == 8 || bits == 16 || bits == 32) return bits;
+    if (bits == ORC_BITS_BF16) return 16;
     return 0;
 }
 
@@ -188,6 +239,7 @@ double orc_decode_field(int bits, uint32_t f, double s)
         return (double)q * s;
     }
     if (bits == 16) return (double)orc_f16_to_f32((uint16_t)f);
+    if (bits == ORC_BITS_BF16) return (double)orc_bf16_to_f32((uint16_t)f);
     float x;
     memcpy(&x, &f, 4);
     return (double)x;
@@ -213,6 +265,7 @@ uint32_t orc_encode_field(int bits, double x, double s)
     if (bits == 4 || bits == 6 || bits == 8)
         return (uint32_t)(orc_quantize(bits, x, s) + (1 << (bits - 1)));
     if (bits == 16) return orc_f32_to_f16((float)x);
+    if (bits == ORC_BITS_BF16) return orc_f32_to_bf16((float)x);
     float y = (float)x;
     uint32_t u;
     memcpy(&u, &y, 4);
@@ -527,6 +580,16 @@ void orc_bruteforce(int dk, int dv, int T, const double *S0, const double *q, co
 void orc_f32_to_f16_array(const float *x, uint16_t *h, long n)
 {
     for (long e = 0; e < n; e++) h[e] = orc_f32_to_f16(x[e]);
+}
+
+void orc_f32_to_bf16_array(const float *x, uint16_t *h, long n)
+{
+    for (long i = 0; i < n; i++) h[i] = orc_f32_to_bf16(x[i]);
+}
+
+void orc_bf16_to_f32_array(const uint16_t *h, float *x, long n)
+{
+    for (long i = 0; i < n; i++) x[i] = orc_bf16_to_f32(h[i]);
 }
 
 void orc_f16_to_f32_array(const uint16_t *h, float *x, long n)

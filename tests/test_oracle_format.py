@@ -202,3 +202,58 @@ def test_encode_decode_tile_roundtrip(orc):
         S = orc.decode_tile(bits, dk, dv, tile, r, c)
         want = vals.astype(np.float16 if bits == 16 else np.float32).astype(np.float64)
         assert np.array_equal(S, want)
+
+
+# ---------------------------------------------------------------- bfloat16 state
+
+def test_bf16_to_f32_exhaustive(orc):
+    """Every bfloat16 pattern: the oracle's decoding equals the pattern placed in
+    the upper half of a binary32 (bfloat16 is that half) and torch's bfloat16."""
+    import torch
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.bf16_bits_to_f32(h)
+    upper = (h.astype(np.uint32) << 16).view(np.float32)
+    via_torch = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(upper)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(np.isnan(via_torch), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), upper[~nan].view(np.uint32))
+    assert np.array_equal(got[~nan].view(np.uint32), via_torch[~nan].view(np.uint32))
+
+
+def test_f32_to_bf16_round_half_even_matches_torch(orc):
+    import torch
+    rng = np.random.default_rng(21)
+    u = rng.integers(0, 2 ** 32, 400_000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    # exact ties (low 16 bits = 0x8000) with even and odd kept halves, the
+    # overflow edge, subnormals and zeros
+    ties = ((rng.integers(0, 2 ** 16, 20_000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    edge = np.array([3.3895313892515355e38, 3.3961775292304172e38, 3.4e38, -3.39e38, 1e-40, -1e-45,
+                     0.0, -0.0, 1.0, 1.00390625, 1.005859375], np.float32)
+    x = np.concatenate([x, ties[np.isfinite(ties)], edge])
+    got = orc.f32_to_bf16_bits(x)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    # NaN stays NaN, infinities stay infinite
+    special = orc.f32_to_bf16_bits(np.array([np.nan, np.inf, -np.inf], np.float32))
+    assert (special[0] & 0x7f80) == 0x7f80 and (special[0] & 0x7f) != 0
+    assert special[1] == 0x7f80 and special[2] == 0xff80
+
+
+def test_bf16_state_tile_roundtrip(orc):
+    rng = np.random.default_rng(22)
+    dk, dv = 12, 20
+    r, c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+    vals = rng.standard_normal((dk, dv)) * 10.0
+    assert orc.field_width(orc.BITS_BF16) == 16 and orc.tile_bytes(orc.BITS_BF16, dk, dv) == dk * dv * 2
+    tile = orc.encode_tile(orc.BITS_BF16, dk, dv, vals, r, c)
+    S = orc.decode_tile(orc.BITS_BF16, dk, dv, tile, r, c)
+    want = orc.bf16_bits_to_f32(orc.f32_to_bf16_bits(vals.astype(np.float32))).astype(np.float64)
+    assert np.array_equal(S, want)
+    # field (i, j) is the bfloat16 of element (i, j) at the layout position
+    for (i, j) in [(0, 0), (5, 7), (11, 19)]:
+        assert orc.field_get(tile, 16, orc.elem_index(i, j, dv)) == \
+            int(orc.f32_to_bf16_bits(np.array([vals[i, j]], np.float32))[0])
+    off, slab = orc.pool_layout([orc.BITS_BF16, 4], 128, 128)
+    assert list(off) == [0, 32768] and slab == 32768 + 8192

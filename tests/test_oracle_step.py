@@ -265,6 +265,33 @@ def test_P3_pivot_is_fp16_of_fp32_path(orc):
                           S32.astype(np.float16).astype(np.float64))
 
 
+def test_bf16_state_is_bf16_of_fp32_path(orc):
+    """The BF16-state step equals the FP32-state step rounded to bfloat16
+    (torch's round-half-even conversion), and reads out the same o."""
+    import torch
+    rng = np.random.default_rng(71)
+    dk, dv = 16, 16
+    S = torch.from_numpy(rng.standard_normal((dk, dv)).astype(np.float32)).bfloat16().double().numpy()
+    r, c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+    B = orc.BITS_BF16
+    tb, t32 = orc.encode_tile(B, dk, dv, S, r, c), orc.encode_tile(32, dk, dv, S, r, c)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv))
+    nb, ob = orc.step_tile(B, dk, dv, tb, r, c, q, k, v, 0.9, 0.4)
+    n32, o32 = orc.step_tile(32, dk, dv, t32, r, c, q, k, v, 0.9, 0.4)
+    assert np.array_equal(ob, o32)
+    S32 = torch.from_numpy(orc.decode_tile(32, dk, dv, n32, r, c).astype(np.float32))
+    assert np.array_equal(orc.decode_tile(B, dk, dv, nb, r, c), S32.bfloat16().double().numpy())
+    # write into a row, as I2: row m becomes bf16(v), other rows untouched
+    m = 3
+    kk = np.zeros(dk, np.float32)
+    kk[m] = 1
+    t2, _ = orc.step_tile(B, dk, dv, tb, r, c, q, kk, v, 1.0, 1.0)
+    after = orc.decode_tile(B, dk, dv, t2, r, c)
+    assert np.array_equal(np.delete(after, m, 0), np.delete(S, m, 0))
+    assert np.array_equal(after[m], torch.from_numpy(v).bfloat16().double().numpy())
+
+
 def test_nonfinite_inputs_follow_the_stated_rule(orc):
     rng = np.random.default_rng(80)
     dk, dv = 16, 16
