@@ -44,8 +44,10 @@ def kernel_source_sha() -> str:
 def algorithmic_bytes_per_step(w, bits) -> int:
     """State read + write of every tile, plus per head-token q, k, v (bf16),
     alpha, beta (fp32) and o (fp32)."""
+    from quantized_recurrent_state_gated_amd.inputs import field_width
+
     d2 = w.dk * w.dv
-    state = sum(2 * d2 * int(b) // 8 for b in bits) * w.n_req
+    state = sum(2 * d2 * field_width(b) // 8 for b in bits) * w.n_req
     io = w.n_req * w.n_heads * (2 * (2 * w.dk + w.dv) + 8 + 4 * w.dv)
     return state + io
 
@@ -125,14 +127,15 @@ def trace_summary(stats_csv: str) -> int:
     return 0
 
 
-def fp32_state_baseline(sq, I, w, dev, stream, ins, quant_ms, steps=16, warmup=10):
-    """The same step with every head holding an unquantized FP32 state (the
-    'FP32 state' baseline of the pages' efficiency comparison), timed on the
-    same inputs; context for the quantized step, not part of the metric."""
+def unquantized_baseline(sq, I, w, dev, stream, ins, quant_ms, fmt=32, steps=16, warmup=10):
+    """The same step with every head holding an unquantized state: FP32 (the
+    'FP32 state' baseline of the pages' efficiency comparison) or bfloat16
+    (fmt = 144), timed on the same inputs; context for the quantized step, not
+    part of the metric."""
     import numpy as np
     import torch
 
-    bits = np.full(w.n_heads, 32, np.uint8)
+    bits = np.full(w.n_heads, fmt, np.uint8)
     nbytes = sq.sq_pool_bytes(w.n_req, w.n_heads, w.dk, w.dv, bits)
     ones_r = torch.ones(w.n_heads, w.dk, device=dev)
     ones_c = torch.ones(w.n_heads, w.dv, device=dev)
@@ -160,9 +163,11 @@ def fp32_state_baseline(sq, I, w, dev, stream, ins, quant_ms, steps=16, warmup=1
     byts = algorithmic_bytes_per_step(w, bits)
     del pool, state
     torch.cuda.empty_cache()
-    return {"ms_per_step": ms, "hbm_gbps": byts / (ms / 1e3) / 1e9, "pool_bytes": nbytes,
-            "speedup_of_quantized_step": ms / quant_ms,
-            "pages_context": "2.91x state-update speedup at 6 bits on NVIDIA A800"}
+    out = {"ms_per_step": ms, "hbm_gbps": byts / (ms / 1e3) / 1e9, "pool_bytes": nbytes,
+           "speedup_of_quantized_step": ms / quant_ms}
+    if fmt == 32:
+        out["pages_context"] = "2.91x state-update speedup at 6 bits on NVIDIA A800"
+    return out
 
 
 def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, steps=32,
@@ -361,7 +366,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-baseline", action="store_true",
-                    help="skip timing the unquantized FP32-state step at the same shape")
+                    help="skip timing the unquantized FP32- and BF16-state steps at the same shape")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip timing a device-to-device copy as a practical bandwidth ceiling")
     ap.add_argument("--small-batch", action="store_true",
@@ -524,9 +529,10 @@ def main() -> int:
             f"({result['channel_gate_step']['frac']:.3f} of HBM peak)")
 
     if not args.no_fp32_baseline:
-        result["fp32_state_baseline"] = fp32_state_baseline(sq, I, w, dev, stream, ins, ms_per_step)
-        log(f"[bench] FP32-state step: {result['fp32_state_baseline']['ms_per_step']:.3f} ms "
-            f"({result['fp32_state_baseline']['speedup_of_quantized_step']:.2f}x)")
+        for key, fmt in (("fp32_state_baseline", 32), ("bf16_state_baseline", I.BITS_BF16)):
+            result[key] = unquantized_baseline(sq, I, w, dev, stream, ins, ms_per_step, fmt)
+            log(f"[bench] {key}: {result[key]['ms_per_step']:.3f} ms "
+                f"({result[key]['speedup_of_quantized_step']:.2f}x)")
 
     if not args.no_cpu_baseline:
         del ins

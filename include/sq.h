@@ -27,7 +27,10 @@
  *              unsigned field q + 2^(b-1);
  *     16       FP16 "pivot" head, IEEE binary16, unquantized ([P1] 方法;
  *              [P5] 时间维度: the riskiest heads stay FP16);
- *     32       FP32 state, unquantized (the full-precision baseline path).
+ *     32       FP32 state, unquantized (the full-precision baseline path);
+ *     144      (SQ_BITS_BF16) bfloat16 state, unquantized, 16-bit fields: a
+ *              16-bit baseline beside the FP32 state, not a format of the
+ *              pages; S' is rounded to bfloat16 (half to even).
  *   Dequantization uses a per-key-row factor times a per-value-column factor
  *   ([P5] 空间维度; [P1] 方法): S^_ij = q_ij * s_ij, s_ij = fl32(r_i * c_j).
  *   Requantization: q = clamp(rne(S'_ij / s_ij), -Q, Q) (round half to even).
@@ -36,7 +39,8 @@
  *       n = 16 * ((i/4) * (d_v/4) + j/4) + 4 * (j%4) + (i%4)
  *   (4x4 blocks in block-row order; inside a block the four rows of a column
  *   are consecutive), and field n occupies bits [n*w, n*w + w) of the tile
- *   read as a little-endian bit stream, w = head_bits[h].  So 4-bit codes sit
+ *   read as a little-endian bit stream, w = head_bits[h] (16 for
+ *   SQ_BITS_BF16).  So 4-bit codes sit
  *   two per byte and 6-bit codes four per three bytes; a tile is
  *   d_k*d_v*w/8 bytes.  A slot's slab holds heads 0..H-1 in order, each tile
  *   starting on a 256-byte boundary; slot p's slab starts at p * slab_bytes.
@@ -71,10 +75,12 @@ extern "C" {
 
 typedef struct sq_pool sq_pool; /* opaque handle */
 
+#define SQ_BITS_BF16 144 /* head_bits value of a bfloat16 state */
+
 typedef enum {
     SQ_OK = 0,
     SQ_ERR_INVALID = -1,     /* null pointer, bad size, misaligned pointer, buffer too small */
-    SQ_ERR_UNSUPPORTED = -2, /* bit width not in {4,6,8,16,32}, or d_k/d_v not supported */
+    SQ_ERR_UNSUPPORTED = -2, /* head_bits not in {4,6,8,16,32,144}, or d_k/d_v not supported */
     SQ_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
     SQ_ERR_NOMEM = -4        /* host or device allocation of the pool's tables failed */
 } sq_status;
@@ -88,9 +94,9 @@ typedef struct {
     int32_t n_slots;          /* number of resident request states (slots), >= 1 */
     int32_t n_heads;          /* recurrent heads per request, >= 1 */
     int32_t d_k, d_v;         /* state rows (key dims) and columns (value dims) */
-    const uint8_t *head_bits; /* HOST [n_heads], each in {4, 6, 8, 16, 32}; copied */
+    const uint8_t *head_bits; /* HOST [n_heads], each in {4, 6, 8, 16, 32, 144}; copied */
     const float *row_scale;   /* DEVICE [n_heads][d_k] fp32, r_i > 0; borrowed, read by
-                                 every call; entries of 16/32-bit heads are ignored */
+                                 every call; entries of unquantized heads are ignored */
     const float *col_scale;   /* DEVICE [n_heads][d_v] fp32, c_j > 0; as row_scale */
     void *state;              /* DEVICE, 256-byte aligned, >= sq_pool_bytes(...) bytes,
                                  laid out as described above; borrowed */

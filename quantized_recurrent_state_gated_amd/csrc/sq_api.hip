@@ -20,14 +20,19 @@
 
 namespace {
 
-constexpr int kClasses[5] = {4, 6, 8, 16, 32};
+// head_bits values: 4/6/8-bit codes, FP16 pivots, FP32 states, BF16 states
+constexpr int kNumClasses = 6;
+constexpr int kClasses[kNumClasses] = {4, 6, 8, 16, 32, SQ_BITS_BF16};
+constexpr int kClassF32 = 4, kClassBF16 = 5;
 
 int class_index(int bits)
 {
-    for (int c = 0; c < 5; c++)
+    for (int c = 0; c < kNumClasses; c++)
         if (kClasses[c] == bits) return c;
     return -1;
 }
+
+int field_width(int bits) { return bits == SQ_BITS_BF16 ? 16 : bits; }
 
 bool shape_ok(int32_t dk, int32_t dv)
 {
@@ -36,7 +41,7 @@ bool shape_ok(int32_t dk, int32_t dv)
 
 uint64_t tile_bytes(int bits, int32_t dk, int32_t dv)
 {
-    return (uint64_t)dk * (uint64_t)dv * (uint64_t)bits / 8;
+    return (uint64_t)dk * (uint64_t)dv * (uint64_t)field_width(bits) / 8;
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -75,8 +80,8 @@ struct sq_pool {
     int64_t *d_off;
     uint8_t *d_bits;
     int32_t *d_stamps;        // sq_check_slots' per-slot stamps + generation, zeroed at alloc
-    int32_t *d_heads[5];
-    int32_t n_class[5];
+    int32_t *d_heads[kNumClasses];
+    int32_t n_class[kNumClasses];
 };
 
 extern "C" {
@@ -126,8 +131,8 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     memcpy(img.data(), off.data(), H * 8);
     int32_t *heads = reinterpret_cast<int32_t *>(img.data() + H * 8);
     size_t pos = 0;
-    size_t start[5];
-    for (int c = 0; c < 5; c++) {
+    size_t start[kNumClasses];
+    for (int c = 0; c < kNumClasses; c++) {
         start[c] = pos;
         p->n_class[c] = 0;
         for (int32_t h = 0; h < d.n_heads; h++)
@@ -152,7 +157,7 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     }
     p->d_off = static_cast<int64_t *>(p->dtab);
     int32_t *dheads = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(p->dtab) + H * 8);
-    for (int c = 0; c < 5; c++) p->d_heads[c] = dheads + start[c];
+    for (int c = 0; c < kNumClasses; c++) p->d_heads[c] = dheads + start[c];
     p->d_bits = static_cast<unsigned char *>(p->dtab) + H * 12;
     p->d_stamps = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(p->dtab) + stamps_at);
     *out = p;
@@ -196,29 +201,32 @@ static sqk::StepArgs base_args(const sq_pool *p, const int32_t *slot_ids)
 static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16, int32_t n_req,
                        void *stream)
 {
-    // d = 128: one launch over all tiles in pool order; otherwise one launch
-    // per width class, widest tiles first
-    static const int order[5] = {4, 3, 2, 1, 0};
+    // d = 128: one launch over the 4/6/8/16-bit tiles in pool order, plus one
+    // per wide class (FP32, BF16 states); otherwise one launch per width
+    // class, widest tiles first
+    static const int order[kNumClasses] = {kClassF32, kClassBF16, 3, 2, 1, 0};
     const bool step_or_read = op == sqk::OP_STEP || op == sqk::OP_STEP_KDA || op == sqk::OP_READOUT;
     if (step_or_read && p->dk == 128 && p->dv == 128) {
         const uint64_t total = (uint64_t)n_req * (uint64_t)p->n_heads;
         if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
-        if (p->n_class[4] < p->n_heads) {  // any 4/6/8/16-bit heads
+        if (p->n_class[kClassF32] + p->n_class[kClassBF16] < p->n_heads) {  // any 4/6/8/16-bit heads
             sqk::FusedArgs f;
             f.a = a;
             f.head_bits = p->d_bits;
             if (sqk::launch_fused128(op, bf16, f, (uint32_t)total, (hipStream_t)stream) != hipSuccess)
                 return SQ_ERR_HIP;
         }
-        if (p->n_class[4] > 0) {  // FP32 heads
-            a.heads = p->d_heads[4];
-            a.Hc = p->n_class[4];
-            if (sqk::launch_f32_128(op, bf16, a, n_req, (hipStream_t)stream) != hipSuccess)
+        for (int c : {kClassF32, kClassBF16}) {
+            if (p->n_class[c] == 0) continue;
+            a.heads = p->d_heads[c];
+            a.Hc = p->n_class[c];
+            if (sqk::launch_wide128(op, kClasses[c], bf16, a, n_req, (hipStream_t)stream) !=
+                hipSuccess)
                 return SQ_ERR_HIP;
         }
         return SQ_OK;
     }
-    for (int oc = 0; oc < 5; oc++) {
+    for (int oc = 0; oc < kNumClasses; oc++) {
         const int c = order[oc];
         if (p->n_class[c] == 0) continue;
         a.heads = p->d_heads[c];

@@ -75,13 +75,21 @@ __device__ __forceinline__ void ld4<uint16_t>(const uint16_t *p, long i, float (
 // encode() takes the updated value in the same form; codes are clamped to
 // [1, 2^b - 1] (the symmetric range) and rounded half to even.
 
-template <int BITS>
-struct Codec {
-    static constexpr int W = BITS / 2;
-};
+// Format tags are the head_bits values: 4, 6, 8 (codes), 16 (FP16 pivot),
+// 32 (FP32 state) and kBF16 (bfloat16 state).  fw<F>() is the field width.
+constexpr int kBF16 = 144;
+
+template <int F>
+constexpr int fw()
+{
+    return F == kBF16 ? 16 : F;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int BITS>
-__device__ __forceinline__ void decode(const uint32_t (&d)[BITS / 2], float (&f)[16])
+__device__ __forceinline__ void decode(const uint32_t (&d)[fw<BITS>() / 2], float (&f)[16])
 {
     if constexpr (BITS == 8) {
 #pragma unroll
@@ -115,6 +123,11 @@ __device__ __forceinline__ void decode(const uint32_t (&d)[BITS / 2], float (&f)
 #pragma unroll
         for (int e = 0; e < 16; e++)
             f[e] = __half2float(__ushort_as_half((unsigned short)(d[e >> 1] >> (16 * (e & 1)))));
+    } else if constexpr (BITS == kBF16) {
+        // a bfloat16 is the upper half of a binary32
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+            f[e] = __uint_as_float((e & 1) ? (d[e >> 1] & 0xffff0000u) : (d[e >> 1] << 16));
     } else {
 #pragma unroll
         for (int e = 0; e < 16; e++) f[e] = __uint_as_float(d[e]);
@@ -138,7 +151,7 @@ __device__ __forceinline__ float clamp_code(float z)
 }
 
 template <int BITS>
-__device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[BITS / 2])
+__device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[fw<BITS>() / 2])
 {
     if constexpr (BITS == 8) {
 #pragma unroll
@@ -187,6 +200,13 @@ __device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[BITS 
             const uint32_t hi = __half_as_ushort(__float2half_rn(z[2 * w + 1]));
             d[w] = lo | (hi << 16);
         }
+    } else if constexpr (BITS == kBF16) {
+        // round half to even, two values per conversion (v_cvt_pk_bf16_f32)
+#pragma unroll
+        for (int w = 0; w < 8; w++) {
+            const f32x2 x = {z[2 * w], z[2 * w + 1]};
+            d[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 16; e++) d[e] = __float_as_uint(z[e]);
@@ -199,7 +219,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Tile blocks are streamed: read once, written once, never reused by this
 // launch, so they may bypass cache retention (nontemporal hint).
 template <int BITS, bool NT>
-__device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[BITS / 2])
+__device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[fw<BITS>() / 2])
 {
     if constexpr (BITS == 4) {
         const u32x2 *q = reinterpret_cast<const u32x2 *>(p);
@@ -211,7 +231,7 @@ __device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[BITS 
         for (int w = 0; w < 3; w++) d[w] = NT ? __builtin_nontemporal_load(q + w) : q[w];
     } else {
 #pragma unroll
-        for (int w = 0; w < BITS / 2; w += 4) {
+        for (int w = 0; w < fw<BITS>() / 2; w += 4) {
             const u32x4 *q = reinterpret_cast<const u32x4 *>(p + 4 * w);
             const u32x4 x = NT ? __builtin_nontemporal_load(q) : *q;
             d[w] = x.x; d[w + 1] = x.y; d[w + 2] = x.z; d[w + 3] = x.w;
@@ -220,7 +240,7 @@ __device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[BITS 
 }
 
 template <int BITS, bool NT>
-__device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[BITS / 2])
+__device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[fw<BITS>() / 2])
 {
     if constexpr (BITS == 4) {
         u32x2 *q = reinterpret_cast<u32x2 *>(p);
@@ -234,7 +254,7 @@ __device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[BITS
         }
     } else {
 #pragma unroll
-        for (int w = 0; w < BITS / 2; w += 4) {
+        for (int w = 0; w < fw<BITS>() / 2; w += 4) {
             u32x4 *q = reinterpret_cast<u32x4 *>(p + 4 * w);
             const u32x4 x = {d[w], d[w + 1], d[w + 2], d[w + 3]};
             if (NT) __builtin_nontemporal_store(x, q); else *q = x;
@@ -295,10 +315,10 @@ struct Smem128K : Smem128 {
 template <int BITS, typename T, bool UPDATE, bool CHG, typename SM>
 __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM &sm)
 {
-    constexpr int W = BITS / 2;
+    constexpr int W = fw<BITS>() / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
-    constexpr int BLK_BYTES = 2 * BITS;
+    constexpr int BLK_BYTES = 2 * fw<BITS>();
     // code tiles stream with the nontemporal hint (measured faster on gfx950);
     // FP16/FP32 tiles measured faster without it
     constexpr bool NT = QUANT;
@@ -476,7 +496,7 @@ struct HalfPos<16> {
 };
 
 template <int BITS>
-__device__ __forceinline__ void to_halves(const uint32_t (&d)[BITS / 2], uint32_t (&hv)[8])
+__device__ __forceinline__ void to_halves(const uint32_t (&d)[fw<BITS>() / 2], uint32_t (&hv)[8])
 {
     if constexpr (BITS == 8) {
 #pragma unroll
@@ -523,10 +543,10 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
     // TPB threads per tile: RG = TPB / 32 row groups, MB = 32 / RG blocks per thread
     constexpr int RG = TPB / 32, MB = 32 / RG;
     using P = HalfPos<BITS>;
-    constexpr int W = BITS / 2;
+    constexpr int W = fw<BITS>() / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
-    constexpr int BLK_BYTES = 2 * BITS;
+    constexpr int BLK_BYTES = 2 * fw<BITS>();
     constexpr bool NT = QUANT;  // code tiles stream nontemporally (measured faster)
     constexpr float SC0 = P::s0 == 0 ? 1.0f : (P::s0 == -24 ? 16777216.0f : 0.0f);
     constexpr float SC1 = P::s1 == 0 ? 1.0f : (P::s1 == -24 ? 16777216.0f : (P::s1 == -22 ? 4194304.0f : 1048576.0f));
@@ -696,14 +716,15 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) v
     }
 }
 
-template <typename T, bool UPDATE, bool CHG>
-__global__ __launch_bounds__(256) void k_step128_f32(StepArgs a)
+template <int FMT, typename T, bool UPDATE, bool CHG>
+__global__ __launch_bounds__(256) void k_step128_wide(StepArgs a)
 {
+    // FP32- or BF16-state heads of a d = 128 pool (a.heads / a.Hc)
     using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
     __shared__ SM sm;
     const int n = blockIdx.x / a.Hc;
     const int h = a.heads[blockIdx.x - n * a.Hc];
-    tile128_wide<32, T, UPDATE, CHG>(a, n, h, sm);
+    tile128_wide<FMT, T, UPDATE, CHG>(a, n, h, sm);
 }
 
 // ---------------------------------------------------------------- any shape
@@ -730,13 +751,14 @@ __device__ __forceinline__ float field_value(uint32_t f)
     // centred value: code q for 4/6/8 bits, the value for 16/32 bits
     if constexpr (BITS <= 8) return (float)((int)f - (1 << (BITS - 1)));
     else if constexpr (BITS == 16) return __half2float(__ushort_as_half((unsigned short)f));
+    else if constexpr (BITS == kBF16) return __uint_as_float(f << 16);
     else return __uint_as_float(f);
 }
 
 template <int BITS, typename T, bool UPDATE, bool CHG>
 __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
 {
-    constexpr int W = BITS / 2;
+    constexpr int W = fw<BITS>() / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
     __shared__ float sW[256], sG[256], sA[256], sB[256], sL[256];
@@ -795,7 +817,7 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
     for (int B = t; B < nblk; B += 256) {
         const int i0 = 4 * (B / (dv >> 2)), j0 = 4 * (B % (dv >> 2));
         uint32_t dd[W];
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + (long)B * 2 * BITS);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + (long)B * 2 * fw<BITS>());
 #pragma unroll
         for (int w = 0; w < W; w++) dd[w] = src[w];
         float f[16], z[16];
@@ -808,7 +830,7 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
                 z[4 * cj + ri] = fmaf(g, f[4 * cj + ri], fmaf(sA[i0 + ri], sB[j0 + cj], OFF * (1.0f - g)));
             }
         encode<BITS>(z, dd);
-        uint32_t *dst = reinterpret_cast<uint32_t *>(tile + (long)B * 2 * BITS);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(tile + (long)B * 2 * fw<BITS>());
 #pragma unroll
         for (int w = 0; w < W; w++) dst[w] = dd[w];
     }
@@ -823,7 +845,7 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
 template <int BITS>
 __global__ __launch_bounds__(256) void k_store(StepArgs a, long total_blocks)
 {
-    constexpr int W = BITS / 2;
+    constexpr int W = fw<BITS>() / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
@@ -855,7 +877,7 @@ __global__ __launch_bounds__(256) void k_store(StepArgs a, long total_blocks)
         }
     uint32_t dd[W];
     encode<BITS>(z, dd);
-    uint32_t *dst = reinterpret_cast<uint32_t *>(tile + B * 2 * BITS);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(tile + B * 2 * fw<BITS>());
 #pragma unroll
     for (int w = 0; w < W; w++) dst[w] = dd[w];
 }
@@ -869,7 +891,7 @@ __global__ __launch_bounds__(256) void k_store(StepArgs a, long total_blocks)
 template <int BITS>
 __global__ __launch_bounds__(256) void k_load(StepArgs a, float *S, long total_blocks)
 {
-    constexpr int W = BITS / 2;
+    constexpr int W = fw<BITS>() / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
@@ -884,7 +906,7 @@ __global__ __launch_bounds__(256) void k_load(StepArgs a, float *S, long total_b
     const uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
     const int i0 = 4 * (int)(B / (dv >> 2)), j0 = 4 * (int)(B % (dv >> 2));
     uint32_t dd[W];
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + B * 2 * BITS);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + B * 2 * fw<BITS>());
 #pragma unroll
     for (int w = 0; w < W; w++) dd[w] = src[w];
     float f[16];
@@ -937,27 +959,36 @@ static hipError_t launch_t(Op op, int bits, const StepArgs &a, int32_t n_req, hi
     case 8: return launch_bits<8, T>(op, a, n_req, st);
     case 16: return launch_bits<16, T>(op, a, n_req, st);
     case 32: return launch_bits<32, T>(op, a, n_req, st);
+    case kBF16: return launch_bits<kBF16, T>(op, a, n_req, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
-static void f32_128_t(Op op, const StepArgs &a, dim3 grid, hipStream_t st)
+template <int FMT, typename T>
+static void wide128_t(Op op, const StepArgs &a, dim3 grid, hipStream_t st)
 {
     if (op == OP_STEP)
-        hipLaunchKernelGGL((k_step128_f32<T, true, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_step128_wide<FMT, T, true, false>), grid, dim3(256), 0, st, a);
     else if (op == OP_STEP_KDA)
-        hipLaunchKernelGGL((k_step128_f32<T, true, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_step128_wide<FMT, T, true, true>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_step128_f32<T, false, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_step128_wide<FMT, T, false, false>), grid, dim3(256), 0, st, a);
 }
 
-hipError_t launch_f32_128(Op op, bool qkv_bf16, const StepArgs &a, int32_t n_req, hipStream_t st)
+hipError_t launch_wide128(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
+                          hipStream_t st)
 {
     if (n_req <= 0 || a.Hc <= 0) return hipSuccess;
     const dim3 grid((unsigned)((long)n_req * a.Hc));
-    if (qkv_bf16) f32_128_t<uint16_t>(op, a, grid, st);
-    else f32_128_t<float>(op, a, grid, st);
+    if (bits == 32) {
+        if (qkv_bf16) wide128_t<32, uint16_t>(op, a, grid, st);
+        else wide128_t<32, float>(op, a, grid, st);
+    } else if (bits == kBF16) {
+        if (qkv_bf16) wide128_t<kBF16, uint16_t>(op, a, grid, st);
+        else wide128_t<kBF16, float>(op, a, grid, st);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

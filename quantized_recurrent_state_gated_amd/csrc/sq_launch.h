@@ -37,13 +37,14 @@ struct FusedArgs {
 };
 
 // Enqueue `op` for the n_req x Hc tiles of one width class.  bits in
-// {4,6,8,16,32}; qkv_bf16 selects the q/k/v element type.  Returns the HIP
+// {4,6,8,16,32,144}; qkv_bf16 selects the q/k/v element type.  Returns the HIP
 // error of the launch.
 hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
                   hipStream_t stream);
 
-// Step or readout over the FP32 heads (a.heads / a.Hc) of a d = 128 pool.
-hipError_t launch_f32_128(Op op, bool qkv_bf16, const StepArgs &a, int32_t n_req,
+// Step or readout over the FP32 (bits 32) or BF16-state (bits 144) heads
+// (a.heads / a.Hc) of a d = 128 pool.
+hipError_t launch_wide128(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
                           hipStream_t stream);
 
 // Step or readout over the 4/6/8/16-bit tiles of a d = 128 pool in one launch.

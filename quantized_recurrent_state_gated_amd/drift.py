@@ -7,8 +7,8 @@ readout against an FP32-state run of the same decode:
     e[n, h, t] = ||o_fmt - o_fp32||_2 / ||o_fp32||_2
 
 Formats: the workload's mixed 4/6/8-bit allocation with FP16 pivots, uniform
-4-bit (same dual-axis max-abs scales re-derived for 4 bits, no pivots) and
-uniform 8-bit.  This mirrors the pages' comparison of mixed-precision state
+4-bit (same dual-axis max-abs scales re-derived for 4 bits, no pivots),
+uniform 8-bit, and an unquantized bfloat16 state (a 16-bit baseline).  This mirrors the pages' comparison of mixed-precision state
 against uniform INT4 / INT8 ("K1 論文詳解" 實驗結果; "线性注意力状态量化难题"
 数据说话) and the accumulation of error over decode steps (直接量化为什么会翻车,
 时间维度); it is a report, not a correctness gate.  The per-head mean error is
@@ -83,7 +83,8 @@ def report(workload: str = "drift", steps: int | None = None, device: str = "cud
     dev = torch.device(device)
     H = w.n_heads
     formats = {"mixed": I.head_bits(w), "uniform_int4": np.full(H, 4, np.uint8),
-               "uniform_int8": np.full(H, 8, np.uint8)}
+               "uniform_int8": np.full(H, 8, np.uint8),
+               "uniform_bf16": np.full(H, I.BITS_BF16, np.uint8)}
     ref = Run(w, np.full(H, 32, np.uint8), dev)
     runs = {k: Run(w, b, dev) for k, b in formats.items()}
     calib_info = {}
@@ -150,6 +151,8 @@ def report(workload: str = "drift", steps: int | None = None, device: str = "cud
                              for t in sorted({0, 15, 127, 511, 1023, steps - 1}) if t < steps}
         per_head = (head_sum[k] / (steps * w.n_req)).cpu().numpy()
         quant = formats[k] <= 8
+        if quant.sum() < 3:  # an unquantized format: rank over every head
+            quant = np.ones_like(quant)
         out["spearman_head_error_vs_half_life"][k] = spearman(per_head[quant], hl[quant])
     return out
 

@@ -33,6 +33,12 @@ COL_RATIO_TARGET = 19.4
 N_OUTLIER_ROWS = 4
 N_OUTLIER_COLS = 4
 STATE_SIGMA = 0.5  # element std of the non-outlier state
+BITS_BF16 = 144    # head_bits value of a bfloat16 state (16-bit fields)
+
+
+def field_width(bits: int) -> int:
+    """Bits per stored element of a head format (head_bits value)."""
+    return 16 if int(bits) == BITS_BF16 else int(bits)
 
 
 @dataclass(frozen=True)
@@ -119,7 +125,7 @@ def head_bits(w: Workload) -> np.ndarray:
     order = np.argsort(-half_lives(w), kind="stable")
     bits = np.zeros(w.n_heads, np.uint8)
     pos = 0
-    for b in (32, 16, 8, 6, 4):
+    for b in (32, BITS_BF16, 16, 8, 6, 4):
         n = w.counts.get(b, 0)
         bits[order[pos:pos + n]] = b
         pos += n
@@ -300,7 +306,7 @@ def pool_stats(w: Workload) -> dict:
     """Sizes of the workload's pool and per-step traffic at the layout's tile sizes."""
     bits = head_bits(w)
     d2 = w.dk * w.dv
-    tile = [d2 * int(b) // 8 for b in bits]
+    tile = [d2 * field_width(b) // 8 for b in bits]
     slab = sum((t + 255) // 256 * 256 for t in tile)
     qkv_bytes = 2 if w.qkv_dtype == "bf16" else 4
     per_head_tok_io = qkv_bytes * (2 * w.dk + w.dv) + 8 + 4 * w.dv

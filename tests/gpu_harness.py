@@ -12,6 +12,10 @@ oracle always starts from the GPU's own pre-step bytes):
                    error is a few fp32 ulps of the tile's magnitude, not of the
                    (small) result;
   FP32 states      |a - b| <= 2e-6 * max|tile| (a few fp32 ulps of the tile);
+  BF16 states      |a - b| <= 2^-7 |b| + 2^-16 max|tile|: one bfloat16 ulp (at most
+                   2^-7 relative: fp32 evaluation order can move a value across a
+                   rounding boundary) plus the same cancellation floor as pivots,
+                   scaled to bfloat16's precision;
   readout o        per (request, head): max_j |o - o_ref| <= 1e-5 + 1e-3 max_j |o_ref|.
 """
 from __future__ import annotations
@@ -35,7 +39,9 @@ def say(*a):
 
 def unpack_fields(tiles: np.ndarray, w: int) -> np.ndarray:
     """tiles: uint8 [n_tiles, tile_bytes] -> uint32 [n_tiles, n_fields], field n at
-    bits [n*w, n*w+w) of each tile's little-endian bit stream."""
+    bits [n*w, n*w+w) of each tile's little-endian bit stream (w = a head_bits
+    value; the bfloat16 state has 16-bit fields)."""
+    w = I.field_width(w)
     tiles = np.ascontiguousarray(tiles, np.uint8)
     nt = tiles.shape[0]
     if w == 8:
@@ -73,6 +79,8 @@ class Tally:
         self.pivot_maxulp = 0
         self.pivot_worst = 0.0  # max of |a-b| / (1e-3 |b| + 2^-20 max|tile|)
         self.fp32_maxrel = 0.0
+        self.bf16_vals = 0
+        self.bf16_worst = 0.0  # max of |a-b| / (2^-7 |b| + 2^-16 max|tile|)
         self.o_worst = 0.0  # max over tiles of err / (atol + rtol * max|o_ref|)
         self.tiles = 0
 
@@ -87,6 +95,12 @@ class Tally:
             self.codes += d.size
             self.code_mismatch += int((d != 0).sum())
             self.code_maxdiff = max(self.code_maxdiff, int(d.max()))
+        elif bits == I.BITS_BF16:
+            fa = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            fb = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            lim = 2.0 ** -7 * np.abs(fb) + 2.0 ** -16 * np.abs(fb).max(axis=1, keepdims=True)
+            self.bf16_vals += fa.size
+            self.bf16_worst = max(self.bf16_worst, float((np.abs(fa - fb) / np.maximum(lim, 1e-38)).max()))
         elif bits == 16:
             d = np.abs(f16_order_key(a) - f16_order_key(b))
             self.pivot_vals += d.size
@@ -113,6 +127,7 @@ class Tally:
         return (f"tiles={self.tiles} codes={self.codes} mismatch={self.code_mismatch} "
                 f"(match {100 * self.match_rate():.5f}%) maxdiff={self.code_maxdiff} "
                 f"pivot_maxulp={self.pivot_maxulp} pivot_worst={self.pivot_worst:.3f} fp32_maxrel={self.fp32_maxrel:.2e} "
+                f"bf16_worst={self.bf16_worst:.3f} "
                 f"o_worst={self.o_worst:.3f}")
 
     def check(self):
@@ -120,6 +135,7 @@ class Tally:
         assert self.match_rate() >= CODE_MATCH_MIN, self.summary()
         assert self.pivot_worst <= 1.0, self.summary()
         assert self.fp32_maxrel <= 2e-6, self.summary()
+        assert self.bf16_worst <= 1.0, self.summary()
         assert self.o_worst <= 1.0, self.summary()
 
 
@@ -129,7 +145,7 @@ def compare_pools(tally: Tally, gpu_pool: np.ndarray, ref_pool: np.ndarray, head
     head_bits = np.asarray(head_bits)
     for b in sorted(set(int(x) for x in head_bits)):
         hs = np.nonzero(head_bits == b)[0]
-        tb = dk * dv * b // 8
+        tb = dk * dv * I.field_width(b) // 8
         idx = np.array([p * slab + off[h] for p in slots for h in hs], np.int64)
         if idx.size == 0:
             continue

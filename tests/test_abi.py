@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(sq):
 
 def test_pool_bytes_matches_state_format(sq, orc):
     for bits, dk, dv in [([4, 6, 8, 16, 32], 128, 128), ([8] * 4, 16, 16), ([6, 4], 12, 20),
-                         ([4], 4, 4), ([16, 6], 256, 128)]:
+                         ([4], 4, 4), ([16, 6], 256, 128), ([144, 4, 32], 128, 128)]:
         _, slab = orc.pool_layout(bits, dk, dv)
         assert sq.sq_pool_bytes(3, len(bits), dk, dv, bits) == 3 * slab
     # serving shape: 70 x 2304 heads at 568/1136/568 + 32 pivots

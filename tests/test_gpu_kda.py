@@ -30,14 +30,14 @@ def test_kda_layer(sq, orc):
 
 @pytest.mark.parametrize("qkv", ["f32", "bf16"])
 def test_kda_d128_every_width(sq, orc, qkv):
-    w = I.Workload("kmix", 3, 10, 128, 128, 4, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, qkv_dtype=qkv,
+    w = I.Workload("kmix", 3, 12, 128, 128, 4, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2, I.BITS_BF16: 2}, qkv_dtype=qkv,
                    seed=199)
     run_teacher_forced(KdaCase(sq, orc, w, n_slots=5, slots=[4, 1, 2]), w.steps, f"kda-mix-{qkv}")
 
 
 @pytest.mark.parametrize("dk,dv", [(12, 20), (64, 128), (256, 32)])
 def test_kda_other_shapes(sq, orc, dk, dv):
-    w = I.Workload("kshape", 2, 5, dk, dv, 3, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=dk * 7 + dv)
+    w = I.Workload("kshape", 2, 6, dk, dv, 3, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=dk * 7 + dv)
     run_teacher_forced(KdaCase(sq, orc, w), w.steps, f"kda-shape{dk}x{dv}")
 
 
@@ -45,7 +45,7 @@ def test_kda_with_equal_channels_is_the_scalar_step(sq, orc):
     """alpha_i = alpha for every channel: the per-channel step and
     sq_decode_step agree to the parity tolerances (the two kernels round in
     a different order, so bit identity is not expected)."""
-    w = I.Workload("keq", 3, 10, 128, 128, 3, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, seed=211)
+    w = I.Workload("keq", 3, 12, 128, 128, 3, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2, I.BITS_BF16: 2}, seed=211)
     a, b = Case(sq, orc, w), Case(sq, orc, w)
     assert np.array_equal(a.host(), b.host())
     tally = Tally()
@@ -67,7 +67,7 @@ def test_kda_with_equal_channels_is_the_scalar_step(sq, orc):
 def test_kda_zero_write_decays_each_row(sq, orc):
     """beta = 0: every key row decays by its own gate; on FP32 heads the new
     state is exactly fl32(alpha_i S_ij); o = S'^T q."""
-    w = I.Workload("kdecay", 2, 5, 128, 128, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=17)
+    w = I.Workload("kdecay", 2, 6, 128, 128, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=17)
     case = KdaCase(sq, orc, w)
     pre = case.host()
     si = case.inputs(0)

@@ -25,7 +25,7 @@ def sq():
 @pytest.mark.parametrize("name,shape", [("tiny", None), ("layer", (3, 12)), ("any", (2, 5))])
 def test_store_bit_exact(sq, orc, name, shape):
     if name == "any":
-        w = I.Workload("any", 2, 5, 12, 20, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=77)
+        w = I.Workload("any", 2, 6, 12, 20, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=77)
     else:
         w = I.WORKLOADS[name] if shape is None else I.scaled(I.WORKLOADS[name], *shape)
     say(f"store {w.name} {w.n_req}x{w.n_heads} d={w.dk}x{w.dv}")
@@ -40,7 +40,7 @@ def test_store_bit_exact(sq, orc, name, shape):
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (12, 20)])
 def test_load_bit_exact(sq, orc, dk, dv):
-    w = I.Workload("load", 2, 5, dk, dv, 2, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=dk + dv)
+    w = I.Workload("load", 2, 6, dk, dv, 2, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=dk + dv)
     case = Case(sq, orc, w, n_slots=4, slots=[3, 1])
     case.step(I.step_inputs(w, 0))  # load a state that has been through a step
     host = case.host()
@@ -86,19 +86,19 @@ def test_layer_all_steps(sq, orc):
 
 @pytest.mark.parametrize("qkv", ["f32", "bf16"])
 def test_d128_every_width(sq, orc, qkv):
-    w = I.Workload("mix", 3, 10, 128, 128, 4, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, qkv_dtype=qkv,
+    w = I.Workload("mix", 3, 12, 128, 128, 4, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2, I.BITS_BF16: 2}, qkv_dtype=qkv,
                    seed=99)
     run_teacher_forced(Case(sq, orc, w, n_slots=5, slots=[4, 1, 2]), w.steps, f"mix-{qkv}")
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (12, 20), (128, 64), (64, 128), (256, 32), (4, 4)])
 def test_other_shapes(sq, orc, dk, dv):
-    w = I.Workload("shape", 2, 5, dk, dv, 3, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=dk * 1000 + dv)
+    w = I.Workload("shape", 2, 6, dk, dv, 3, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=dk * 1000 + dv)
     run_teacher_forced(Case(sq, orc, w), w.steps, f"shape{dk}x{dv}")
 
 
 def test_single_width_pools(sq, orc):
-    for bits in (4, 6, 8, 16, 32):
+    for bits in (4, 6, 8, 16, 32, I.BITS_BF16):
         w = I.Workload(f"only{bits}", 2, 3, 128, 128, 2, {bits: 3}, seed=bits)
         run_teacher_forced(Case(sq, orc, w), w.steps, w.name)
 
@@ -108,7 +108,7 @@ def test_single_width_pools(sq, orc):
 def test_pure_decay_keeps_codes_and_readout(sq, orc):
     """beta = 0, alpha = 1: codes are unchanged bit for bit, o = S^T q equals
     sq_readout, for every width."""
-    w = I.Workload("decay", 2, 10, 128, 128, 3, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2}, seed=5)
+    w = I.Workload("decay", 2, 12, 128, 128, 3, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2, I.BITS_BF16: 2}, seed=5)
     case = Case(sq, orc, w)
     start = case.host()
     for t in range(w.steps):
@@ -130,7 +130,7 @@ def test_pure_decay_keeps_codes_and_readout(sq, orc):
 
 def test_write_into_row(sq, orc):
     """alpha = beta = 1, k = e_m: only row m changes."""
-    w = I.Workload("row", 1, 5, 128, 128, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1}, seed=6)
+    w = I.Workload("row", 1, 6, 128, 128, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=6)
     case = Case(sq, orc, w)
     pre = case.host()
     si = I.step_inputs(w, 0)
