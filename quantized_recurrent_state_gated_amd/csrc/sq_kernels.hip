@@ -797,7 +797,7 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
         float U = 0.0f, Y = 0.0f;
         for (int i = 0; i < dk; i++) {
             const long nidx = 16L * ((i >> 2) * (dv >> 2) + (j >> 2)) + 4 * (j & 3) + (i & 3);
-            const float x = field_value<BITS>(field_get(tile, BITS, nidx));
+            const float x = field_value<BITS>(field_get(tile, fw<BITS>(), nidx));
             U = fmaf(sW[i], x, U);
             Y = fmaf(sG[i], x, Y);
         }
