@@ -334,3 +334,31 @@ def test_two_pools_on_two_streams(sq, orc):
     torch.cuda.synchronize()
     for c, wnt in zip(cases, want):
         assert torch.equal(c.dev, wnt)
+
+
+def test_saturating_updates(sq, orc):
+    """Writes far outside the scales' range: most codes of the written rows
+    clamp to +-Q, and the clamp decision matches the oracle's."""
+    w = I.Workload("sat", 2, 12, 128, 128, 3, {4: 2, 6: 2, 8: 2, 16: 2, 32: 2, I.BITS_BF16: 2},
+                   seed=41)
+    case = Case(sq, orc, w)
+    tally = Tally()
+    saturated = 0
+    for t in range(w.steps):
+        si = I.step_inputs(w, t)
+        si.v = (si.v.float() * 200.0).to(si.v.dtype)
+        si.beta.fill_(1.0)
+        pre = case.host()
+        o = case.step(si)
+        post = case.host()
+        ref, o_ref = case.oracle_step(pre, si)
+        case.compare(tally, post, ref)
+        tally.add_o(o.cpu().numpy(), o_ref)
+        for h in range(w.n_heads):
+            b = int(case.bits[h])
+            if b <= 8:
+                tb = orc.tile_bytes(b, 128, 128)
+                f = unpack_fields(post[None, int(case.off[h]):int(case.off[h]) + tb], b)
+                saturated += int(((f == 1) | (f == 2 ** b - 1)).sum())
+    tally.check()
+    assert saturated > 1000  # the clamp path was exercised
