@@ -78,8 +78,9 @@ def _pmc_rows(path, counter):
     rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
     step = [float(r["Counter_Value"]) * 1024 for r in rows if STEP_KERNEL in r["Kernel_Name"]]
     kda = [float(r["Counter_Value"]) * 1024 for r in rows if KDA_KERNEL in r["Kernel_Name"]]
-    copies = [float(r["Counter_Value"]) * 1024 for r in rows
-              if "copyBuffer" in r["Kernel_Name"] or "copy_kernel" in r["Kernel_Name"]]
+    # the calibration copy is the runtime's blit kernel; torch's own copy and
+    # conversion kernels (other sizes) must not be taken for it
+    copies = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
     return step, kda, copies
 
 

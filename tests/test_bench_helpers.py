@@ -27,10 +27,13 @@ def test_pmc_summary_scales_by_the_copy_and_picks_exact_kernels(tmp_path, monkey
     f32 = "void sqk::k_step128_f32<unsigned short, true, false>(sqk::StepArgs)"
     copy = "__amd_rocclr_copyBuffer"
     gib = 1 << 20  # KiB in 1 GiB
+    conv = "void at::native::vectorized_elementwise_kernel<4, at::native::copy_kernel_impl>"
     _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE",
-             [(copy, gib / 2), (step, 1000), (step, 1002), (step, 998), (kda, 1100), (f32, 9e9)])
+             [(copy, 3), (copy, gib / 2), (step, 1000), (step, 1002), (step, 998), (kda, 1100),
+              (f32, 9e9), (conv, 5e9)])
     _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE",
-             [(copy, gib), (step, 2000), (step, 2000), (kda, 2000), (f32, 9e9)])
+             [(copy, 2), (copy, gib), (step, 2000), (step, 2000), (kda, 2000), (f32, 9e9),
+              (conv, 5e9)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     assert bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv")) == 0
