@@ -92,10 +92,24 @@ uint64_t sq_pool_bytes(int32_t n_slots, int32_t n_heads, int32_t d_k, int32_t d_
     uint64_t slab = 0;
     if (n_slots < 1) return 0;
     if (layout(n_heads, d_k, d_v, head_bits, nullptr, &slab) != SQ_OK) return 0;
+    if (slab > UINT64_MAX / (uint64_t)n_slots) return 0;  // does not fit in 64 bits
     return slab * (uint64_t)n_slots;
 }
 
+static int pool_alloc(const sq_pool_desc *desc, sq_pool **out);
+
 int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
+{
+    // no C++ exception crosses the ABI: a failed host allocation is SQ_ERR_NOMEM
+    try {
+        return pool_alloc(desc, out);
+    } catch (...) {
+        if (out) *out = nullptr;
+        return SQ_ERR_NOMEM;
+    }
+}
+
+static int pool_alloc(const sq_pool_desc *desc, sq_pool **out)
 {
     if (!desc || !out) return SQ_ERR_INVALID;
     *out = nullptr;
@@ -108,7 +122,8 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     uint64_t slab = 0;
     int st = layout(d.n_heads, d.d_k, d.d_v, d.head_bits, &off, &slab);
     if (st != SQ_OK) return st;
-    if (d.state_bytes < slab * (uint64_t)d.n_slots) return SQ_ERR_INVALID;
+    if (slab > UINT64_MAX / (uint64_t)d.n_slots || d.state_bytes < slab * (uint64_t)d.n_slots)
+        return SQ_ERR_INVALID;
 
     sq_pool *p = new (std::nothrow) sq_pool();
     if (!p) return SQ_ERR_NOMEM;
@@ -147,6 +162,7 @@ int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out)
         return SQ_ERR_HIP;
     }
     if (hipMalloc(&p->dtab, img.size()) != hipSuccess) {
+        p->dtab = nullptr;
         delete p;
         return SQ_ERR_NOMEM;
     }
@@ -201,14 +217,18 @@ static sqk::StepArgs base_args(const sq_pool *p, const int32_t *slot_ids)
 static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16, int32_t n_req,
                        void *stream)
 {
+    // every launch must fit a 1-D grid of at most 2^31 - 1 workgroups: one per
+    // tile for the step and readout, one per 256 blocks for store and load
+    const uint64_t tiles = (uint64_t)n_req * (uint64_t)p->n_heads;
+    const uint64_t blocks = tiles * (uint64_t)(p->dk / 4) * (uint64_t)(p->dv / 4);
+    if (tiles > 0x7fffffffu || (blocks + 255) / 256 > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
     // d = 128: one launch over the 4/6/8/16-bit tiles in pool order, plus one
     // per wide class (FP32, BF16 states); otherwise one launch per width
     // class, widest tiles first
     static const int order[kNumClasses] = {kClassF32, kClassBF16, 3, 2, 1, 0};
     const bool step_or_read = op == sqk::OP_STEP || op == sqk::OP_STEP_KDA || op == sqk::OP_READOUT;
     if (step_or_read && p->dk == 128 && p->dv == 128) {
-        const uint64_t total = (uint64_t)n_req * (uint64_t)p->n_heads;
-        if (total > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
+        const uint64_t total = tiles;
         if (p->n_class[kClassF32] + p->n_class[kClassBF16] < p->n_heads) {  // any 4/6/8/16-bit heads
             sqk::FusedArgs f;
             f.a = a;

@@ -87,3 +87,12 @@ def test_null_handles_and_status_strings(sq):
     for s in (0, -1, -2, -3, -4, 7):
         assert isinstance(sq.sq_status_string(s), str) and sq.sq_status_string(s)
     assert sq.sq_status_string(-2) != sq.sq_status_string(-1)
+
+
+def test_pool_bytes_reports_64_bit_overflow_as_invalid(sq):
+    H = 1 << 20
+    bits = [32] * H  # 1 Mi FP32 heads of 256 x 256: 2^38 bytes per slot
+    assert sq.sq_pool_bytes(1, H, 256, 256, bits) == 1 << 38
+    assert sq.sq_pool_bytes((1 << 25) - 1, H, 256, 256, bits) == ((1 << 25) - 1) << 38
+    assert sq.sq_pool_bytes(1 << 26, H, 256, 256, bits) == 0  # 2^64 does not fit
+    assert sq.sq_pool_bytes(2 ** 31 - 1, H, 256, 256, bits) == 0
