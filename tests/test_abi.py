@@ -96,3 +96,17 @@ def test_pool_bytes_reports_64_bit_overflow_as_invalid(sq):
     assert sq.sq_pool_bytes((1 << 25) - 1, H, 256, 256, bits) == ((1 << 25) - 1) << 38
     assert sq.sq_pool_bytes(1 << 26, H, 256, 256, bits) == 0  # 2^64 does not fit
     assert sq.sq_pool_bytes(2 ** 31 - 1, H, 256, 256, bits) == 0
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    """include/sq.h is a C header: a C99 translation unit using every entry
+    point compiles without C++."""
+    import subprocess
+    src = tmp_path / "use.c"
+    names = _declared()
+    src.write_text('#include "sq.h"\ntypedef void (*fn)(void);\nfn table[] = {' +
+                   ", ".join(f"(fn){n}" for n in names) +
+                   "};\nint main(void) { return SQ_OK + SQ_F32 + SQ_BITS_BF16 - 144; }\n")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                        f"-I{os.path.join(ROOT, 'include')}", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
