@@ -283,6 +283,31 @@ __device__ __forceinline__ float wave_sum(float x)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
+// ---------------------------------------------------------------- XCD-aware tile order
+//
+// The dispatcher deals workgroups to the 8 XCDs of an MI355X round-robin
+// (workgroup g runs on XCD g % 8).  Over a long launch the XCDs drift apart,
+// and with tile = workgroup the eight XCDs end up streaming from eight
+// scattered parts of one shared address window.  Instead XCD x is given the
+// contiguous x-th eighth of the tiles, which it walks in order: eight compact
+// sequential streams.  Measured on 70 x 2304 serving-mix pools: neutral at 70
+// requests (5.84 TB/s), +8 % at 128 and +10 % at 256 requests, where the
+// round-robin order fell to 5.3 TB/s.  The grid is rounded up to a multiple
+// of 8; surplus workgroups exit at once.
+
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t n_tiles)
+{
+    const uint32_t per = (n_tiles + kXcds - 1) / kXcds;
+    return (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;  // >= n_tiles: no tile
+}
+
+__host__ __forceinline__ uint32_t xcd_grid(uint32_t n_tiles)
+{
+    return (n_tiles + kXcds - 1) / kXcds * kXcds;
+}
+
 // ---------------------------------------------------------------- d = 128 step
 //
 // Shared memory of one tile.  Two bodies use it: tile128 (the fused launch
@@ -698,13 +723,14 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
 template <typename T, bool UPDATE, bool CHG, int TPB, int WPE>
 __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void k_step128(FusedArgs f)
 {
-    // block b is request b / H, head b % H: the grid walks the pool in memory
-    // order, so tiles of every width are interleaved on each CU (VALU-heavy
-    // narrow codes overlap with memory-heavy wide tiles).  FP32 heads are
-    // skipped here and run in k_step128_f32.
+    // tile b is request b / H, head b % H: each XCD walks its part of the pool
+    // in memory order, so tiles of every width are interleaved on each CU
+    // (VALU-heavy narrow codes overlap with memory-heavy wide tiles).  FP32-
+    // and BF16-state heads are skipped here and run in k_step128_wide.
     using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
     __shared__ SM sm;
-    const uint32_t b = blockIdx.x;
+    const uint32_t b = xcd_tile(f.n_tiles);
+    if (b >= f.n_tiles) return;
     const int n = (int)(b / (uint32_t)f.a.H);
     const int h = (int)(b - (uint32_t)n * (uint32_t)f.a.H);
     switch (f.head_bits[h]) {
@@ -722,8 +748,11 @@ __global__ __launch_bounds__(256) void k_step128_wide(StepArgs a)
     // FP32- or BF16-state heads of a d = 128 pool (a.heads / a.Hc)
     using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
     __shared__ SM sm;
-    const int n = blockIdx.x / a.Hc;
-    const int h = a.heads[blockIdx.x - n * a.Hc];
+    const uint32_t n_tiles = (uint32_t)a.n_req * (uint32_t)a.Hc;
+    const uint32_t b = xcd_tile(n_tiles);
+    if (b >= n_tiles) return;
+    const int n = (int)(b / (uint32_t)a.Hc);
+    const int h = a.heads[b - (uint32_t)n * (uint32_t)a.Hc];
     tile128_wide<FMT, T, UPDATE, CHG>(a, n, h, sm);
 }
 
@@ -979,13 +1008,15 @@ hipError_t launch_wide128(Op op, int bits, bool qkv_bf16, const StepArgs &a, int
                           hipStream_t st)
 {
     if (n_req <= 0 || a.Hc <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((long)n_req * a.Hc));
+    StepArgs b = a;
+    b.n_req = n_req;
+    const dim3 grid(xcd_grid((uint32_t)((long)n_req * a.Hc)));
     if (bits == 32) {
-        if (qkv_bf16) wide128_t<32, uint16_t>(op, a, grid, st);
-        else wide128_t<32, float>(op, a, grid, st);
+        if (qkv_bf16) wide128_t<32, uint16_t>(op, b, grid, st);
+        else wide128_t<32, float>(op, b, grid, st);
     } else if (bits == kBF16) {
-        if (qkv_bf16) wide128_t<kBF16, uint16_t>(op, a, grid, st);
-        else wide128_t<kBF16, float>(op, a, grid, st);
+        if (qkv_bf16) wide128_t<kBF16, uint16_t>(op, b, grid, st);
+        else wide128_t<kBF16, float>(op, b, grid, st);
     } else {
         return hipErrorInvalidValue;
     }
@@ -1014,10 +1045,12 @@ hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_
                           hipStream_t st)
 {
     if (n_blocks == 0) return hipSuccess;
-    const dim3 grid(n_blocks);
+    FusedArgs g = f;
+    g.n_tiles = n_blocks;
+    const dim3 grid(xcd_grid(n_blocks));
     // two waves per tile, each thread holding eight 4x4 blocks as packed
     // halves; the register budget is held to 5 waves per SIMD
-    fused128<128, 5>(op, qkv_bf16, f, grid, st);
+    fused128<128, 5>(op, qkv_bf16, g, grid, st);
     return hipGetLastError();
 }
 

@@ -24,16 +24,18 @@ struct StepArgs {
     const float *beta;         // [n_req][H]
     float *o;                  // [n_req][H][dv] or null
     const float *S;            // store: source, load: destination, [n_req][H][dk][dv]
+    int32_t n_req;             // requests in the batch (set by the launchers that need it)
 };
 
 // OP_STEP_KDA is the step with a per-key-channel gate (alpha [n_req][H][dk]).
 enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2, OP_LOAD = 3, OP_STEP_KDA = 4 };
 
-// One launch over every tile of a d_k = d_v = 128 pool: block b is request
+// One launch over every tile of a d_k = d_v = 128 pool: tile b is request
 // b / H, head b % H, whose width is head_bits[h].
 struct FusedArgs {
     StepArgs a;
     const uint8_t *head_bits;  // [H], device
+    uint32_t n_tiles;          // n_req * H
 };
 
 // Enqueue `op` for the n_req x Hc tiles of one width class.  bits in
