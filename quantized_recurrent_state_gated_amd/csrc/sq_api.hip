@@ -221,7 +221,9 @@ static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16,
     // tile for the step and readout, one per 256 blocks for store and load
     const uint64_t tiles = (uint64_t)n_req * (uint64_t)p->n_heads;
     const uint64_t blocks = tiles * (uint64_t)(p->dk / 4) * (uint64_t)(p->dv / 4);
-    if (tiles > 0x7fffffffu || (blocks + 255) / 256 > 0x7fffffffu) return SQ_ERR_UNSUPPORTED;
+    // (the d = 128 launches round each request's heads up to a multiple of 8)
+    if (tiles + 8 * (uint64_t)n_req > 0x7fffffffu || (blocks + 255) / 256 > 0x7fffffffu)
+        return SQ_ERR_UNSUPPORTED;
     // d = 128: one launch over the 4/6/8/16-bit tiles in pool order, plus one
     // per wide class (FP32, BF16 states); otherwise one launch per width
     // class, widest tiles first

@@ -35,7 +35,6 @@ enum Op { OP_STEP = 0, OP_READOUT = 1, OP_STORE = 2, OP_LOAD = 3, OP_STEP_KDA = 
 struct FusedArgs {
     StepArgs a;
     const uint8_t *head_bits;  // [H], device
-    uint32_t n_tiles;          // n_req * H
 };
 
 // Enqueue `op` for the n_req x Hc tiles of one width class.  bits in
