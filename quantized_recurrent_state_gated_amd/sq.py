@@ -127,6 +127,7 @@ class SqPool:
                  head_bits):
         self.handle = handle
         self._keep = keep
+        self._free = _lib.sq_pool_free  # the library that made the handle releases it
         self.n_slots, self.n_heads, self.d_k, self.d_v = n_slots, n_heads, d_k, d_v
         self.head_bits = list(int(b) for b in head_bits)
 
@@ -135,7 +136,14 @@ class SqPool:
         return self._keep[0]
 
     def __del__(self):
-        sq_pool_free(self)
+        # also runs at interpreter exit, when module globals may already be gone
+        handle, free = getattr(self, "handle", None), getattr(self, "_free", None)
+        if handle and free is not None:
+            try:
+                free(handle)
+            except Exception:
+                pass
+        self.handle = None
 
 
 def sq_pool_alloc(n_slots: int, n_heads: int, d_k: int, d_v: int, head_bits, row_scale,
@@ -154,7 +162,7 @@ def sq_pool_alloc(n_slots: int, n_heads: int, d_k: int, d_v: int, head_bits, row
 
 def sq_pool_free(pool: SqPool) -> None:
     if pool is not None and getattr(pool, "handle", None):
-        _lib.sq_pool_free(pool.handle)
+        pool._free(pool.handle)
         pool.handle = None
 
 
