@@ -172,7 +172,7 @@ def unquantized_baseline(sq, I, w, dev, stream, ins, quant_ms, fmt=32, steps=16,
 
 
 def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, steps=32,
-                      warmup=10):
+                      warmup=40):
     """The per-key-channel-gate (KDA) step, sq_decode_step_kda, on the same pool
     and inputs with alpha [n_req][H][d_k] resident in HBM: the second model
     family's step at the same shape.  Reported beside the metric, not in it."""
@@ -358,8 +358,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=20,
-                    help="untimed steps first; launch times settle after ~10-15 launches")
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first: after an idle spell launch times jump and take "
+                         "~25-30 launches to settle")
     ap.add_argument("--workload", default="serving", choices=["serving", "highconc", "layer", "drift"])
     ap.add_argument("--distinct-inputs", type=int, default=16,
                     help="distinct pre-generated step inputs, cycled over the timed steps")
