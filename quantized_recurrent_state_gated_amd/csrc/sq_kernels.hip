@@ -647,6 +647,14 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
 #pragma unroll
     for (int m = 0; m < MB; m++) to_halves<BITS>(d[m], hv[m]);
 
+    // The two reductions (pass 1, then the column finalisation) run at a
+    // raised wave priority: a tile whose data has arrived gets through its two
+    // barriers sooner, while other waves on the SIMD are still waiting for
+    // memory.  Measured on 70 x 2304 pools: -1.9 % per step on the serving
+    // mix, -3.7 % all-6-bit, -4.5 % on the 4-bit-heavy mix; raising it from
+    // the start of the tile instead gained nothing.
+    __builtin_amdgcn_s_setprio(2);
+
     // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
     float pu[4] = {0, 0, 0, 0}, py[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -695,6 +703,7 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
     }
     if (!UPDATE) return;
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     const float4 b4 = *reinterpret_cast<const float4 *>(&sm.b[4 * cb]);
     const float b[4] = {b4.x, b4.y, b4.z, b4.w};
     // the halves are read again in pass 2: keeping them opaque makes the
