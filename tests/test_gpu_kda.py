@@ -106,3 +106,11 @@ def test_kda_host_errors(sq, orc):
     z = torch.zeros(0, device="cuda")
     sq.sq_decode_step_kda(case.pool, empty, z, z, z, z, z, None)
     assert np.array_equal(case.host(), pre)
+
+
+def test_kda_mid_size_launch(sq, orc):
+    """The per-channel gate through the 256-thread launch (1,024-16,383 tiles)."""
+    w = I.Workload("kmid", 4, 300, 128, 128, 2, {4: 96, 6: 100, 8: 96, 16: 4, 32: 2, I.BITS_BF16: 2},
+                   seed=52)
+    assert 1024 <= w.n_req * w.n_heads < 16384
+    run_teacher_forced(KdaCase(sq, orc, w), w.steps, "kda-mid")

@@ -362,3 +362,12 @@ def test_saturating_updates(sq, orc):
                 saturated += int(((f == 1) | (f == 2 ** b - 1)).sum())
     tally.check()
     assert saturated > 1000  # the clamp path was exercised
+
+
+def test_mid_size_launch_takes_256_threads(sq, orc):
+    """1,024-16,383 tiles take the 256-thread launch of the d = 128 step
+    (four blocks per thread): same parity bar, every width, scrambled slots."""
+    w = I.Workload("mid", 4, 400, 128, 128, 3,
+                   {4: 96, 6: 196, 8: 96, 16: 4, 32: 4, I.BITS_BF16: 4}, seed=51)
+    assert 1024 <= w.n_req * w.n_heads < 16384
+    run_teacher_forced(Case(sq, orc, w, n_slots=6, slots=[5, 0, 3, 1]), w.steps, "mid")
