@@ -71,13 +71,16 @@ class Run:
             self.sq.sq_pool_store(self.pool, self.slots[p:p + 1], I.initial_state(w, p, dev))
         self.o = torch.empty(w.n_req, w.n_heads, w.dv, device=dev)
 
-    def step(self, si):
-        self.sq.sq_decode_step(self.pool, self.slots, si.q, si.k, si.v, si.alpha, si.beta, self.o)
+    def step(self, si, kda=False):
+        step = self.sq.sq_decode_step_kda if kda else self.sq.sq_decode_step
+        step(self.pool, self.slots, si.q, si.k, si.v, si.alpha, si.beta, self.o)
         return self.o
 
 
 def report(workload: str = "drift", steps: int | None = None, device: str = "cuda",
-           calibrated: bool = False) -> dict:
+           calibrated: bool = False, kda: bool = False) -> dict:
+    """kda: every run (the FP32 reference included) steps with the per-key-channel
+    gate, alpha from inputs.channel_gates."""
     w = I.WORKLOADS[workload]
     steps = steps or w.steps
     dev = torch.device(device)
@@ -120,10 +123,12 @@ def report(workload: str = "drift", steps: int | None = None, device: str = "cud
     t0 = time.time()
     for t in range(steps):
         si = I.step_inputs(w, t, dev)
-        o_ref = ref.step(si)
+        if kda:
+            si.alpha = I.channel_gates(w, t, dev)
+        o_ref = ref.step(si, kda)
         nref = o_ref.norm(dim=-1).clamp_min(1e-30)
         for k, run in runs.items():
-            e = (run.step(si) - o_ref).norm(dim=-1) / nref  # [n_req, H]
+            e = (run.step(si, kda) - o_ref).norm(dim=-1) / nref  # [n_req, H]
             flat = e.flatten()
             qv = torch.quantile(flat, qs)
             curves[k]["mean"].append(float(flat.mean()))
@@ -140,6 +145,7 @@ def report(workload: str = "drift", steps: int | None = None, device: str = "cud
                      "half_life": list(w.half_life),
                      "mixed_bits": {str(int(b)): int((mixed_bits == b).sum()) for b in sorted(set(mixed_bits))}},
         "reference": "FP32-state run of the same decode (same S0, q/k/v, gates)",
+        "gate": "per-key-channel (KDA reading)" if kda else "scalar per head",
         "metric": "||o - o_fp32||_2 / ||o_fp32||_2 per (request, head), stats over requests x heads",
         "curves": curves,
         "summary": {},
@@ -164,8 +170,10 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=None)
     ap.add_argument("--calibrated", action="store_true",
                     help="also run the calibrated widths and factors (offline calibration)")
+    ap.add_argument("--kda", action="store_true",
+                    help="step every format with the per-key-channel gate")
     a = ap.parse_args(argv)
-    rep = report(a.workload, a.steps, calibrated=a.calibrated)
+    rep = report(a.workload, a.steps, calibrated=a.calibrated, kda=a.kda)
     text = json.dumps(rep)
     if a.out:
         with open(a.out, "w") as f:
