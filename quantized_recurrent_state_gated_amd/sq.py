@@ -98,6 +98,33 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
 
 
+_FLOATS = (torch.float32, torch.bfloat16)
+_DEVICE_TYPES = ("cuda",)  # device types a tensor argument may live on
+
+
+def _arg(x, where: str, name: str, dtypes, numel: int, optional: bool = False) -> None:
+    """Host-side check of a device tensor argument: CUDA, contiguous, one of
+    `dtypes`, `numel` elements.  A size mismatch is SQ_ERR_INVALID (as the
+    library reports for sizes it can check), a wrong dtype a TypeError.  Raw
+    integer pointers are passed through unchecked."""
+    if x is None:
+        if optional:
+            return
+        raise SqError(SQ_ERR_INVALID, f"{where} ({name} is required)")
+    if isinstance(x, int):
+        return
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{where}: {name} must be a torch tensor or a device pointer")
+    if x.dtype not in dtypes:
+        raise TypeError(f"{where}: {name} must be {' or '.join(str(d) for d in dtypes)}, got {x.dtype}")
+    if x.numel() and x.device.type not in _DEVICE_TYPES:
+        raise SqError(SQ_ERR_INVALID, f"{where} ({name} is not on a GPU)")
+    if not x.is_contiguous():
+        raise SqError(SQ_ERR_INVALID, f"{where} ({name} is not contiguous)")
+    if x.numel() != numel:
+        raise SqError(SQ_ERR_INVALID, f"{where} ({name} has {x.numel()} elements, expected {numel})")
+
+
 def _bits_array(head_bits):
     hb = bytes(int(b) for b in head_bits)
     return (ctypes.c_uint8 * max(len(hb), 1)).from_buffer_copy(hb or b"\0"), len(hb)
@@ -107,6 +134,7 @@ def sq_check_slots(pool: SqPool, slot_ids, result, stream=None) -> None:
     """Write into the int32 device tensor `result` 0 for a valid batch, else
     1 (id out of range) | 2 (id repeated)."""
     n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    _arg(result, "sq_check_slots", "result", (torch.int32,), 1)
     _check(_lib.sq_check_slots(pool.handle, _ptr(slot_ids), n_req, _ptr(result), _stream(stream)),
            "sq_check_slots")
 
@@ -173,8 +201,15 @@ def sq_pool_tile_offset(pool: SqPool, slot: int, head: int):
     return int(off.value), int(nb.value)
 
 
+def _state_elems(pool: SqPool, n_req: int) -> int:
+    return n_req * pool.n_heads * pool.d_k * pool.d_v
+
+
 def sq_pool_store(pool: SqPool, slot_ids, S, stream=None) -> None:
     n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    if n_req:
+        _arg(slot_ids, "sq_pool_store", "slot_ids", (torch.int32,), n_req)
+        _arg(S, "sq_pool_store", "S", (torch.float32,), _state_elems(pool, n_req))
     _check(_lib.sq_pool_store(pool.handle, _ptr(slot_ids), n_req, _ptr(S), _stream(stream)),
            "sq_pool_store")
 
@@ -182,14 +217,30 @@ def sq_pool_store(pool: SqPool, slot_ids, S, stream=None) -> None:
 def sq_pool_load(pool: SqPool, slot_ids, S, stream=None) -> None:
     """Dequantize the slots' states into the fp32 device tensor S [n_req][H][dk][dv]."""
     n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    if n_req:
+        _arg(slot_ids, "sq_pool_load", "slot_ids", (torch.int32,), n_req)
+        _arg(S, "sq_pool_load", "S", (torch.float32,), _state_elems(pool, n_req))
     _check(_lib.sq_pool_load(pool.handle, _ptr(slot_ids), n_req, _ptr(S), _stream(stream)),
            "sq_pool_load")
 
 
-def sq_decode_step(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=None) -> None:
+def _step_args(where, pool, slot_ids, q, k, v, alpha, beta, o, alpha_per_channel):
     n_req = int(slot_ids.numel())
     if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k and v must share one dtype")
+        raise TypeError(f"{where}: q, k and v must share one dtype")
+    H, dk, dv = pool.n_heads, pool.d_k, pool.d_v
+    _arg(slot_ids, where, "slot_ids", (torch.int32,), n_req)
+    _arg(q, where, "q", _FLOATS, n_req * H * dk)
+    _arg(k, where, "k", _FLOATS, n_req * H * dk)
+    _arg(v, where, "v", _FLOATS, n_req * H * dv)
+    _arg(alpha, where, "alpha", (torch.float32,), n_req * H * (dk if alpha_per_channel else 1))
+    _arg(beta, where, "beta", (torch.float32,), n_req * H)
+    _arg(o, where, "o", (torch.float32,), n_req * H * dv, optional=True)
+    return n_req
+
+
+def sq_decode_step(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=None) -> None:
+    n_req = _step_args("sq_decode_step", pool, slot_ids, q, k, v, alpha, beta, o, False)
     _check(_lib.sq_decode_step(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _ptr(k), _ptr(v),
                                _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream)),
            "sq_decode_step")
@@ -197,9 +248,7 @@ def sq_decode_step(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=
 
 def sq_decode_step_kda(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, stream=None) -> None:
     """Per-key-channel-gate step; alpha is fp32 [n_req][n_heads][d_k]."""
-    n_req = int(slot_ids.numel())
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k and v must share one dtype")
+    n_req = _step_args("sq_decode_step_kda", pool, slot_ids, q, k, v, alpha, beta, o, True)
     _check(_lib.sq_decode_step_kda(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _ptr(k), _ptr(v),
                                    _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(o),
                                    _stream(stream)), "sq_decode_step_kda")
@@ -207,5 +256,8 @@ def sq_decode_step_kda(pool: SqPool, slot_ids, q, k, v, alpha, beta, o=None, str
 
 def sq_readout(pool: SqPool, slot_ids, q, o, stream=None) -> None:
     n_req = int(slot_ids.numel())
+    _arg(slot_ids, "sq_readout", "slot_ids", (torch.int32,), n_req)
+    _arg(q, "sq_readout", "q", _FLOATS, n_req * pool.n_heads * pool.d_k)
+    _arg(o, "sq_readout", "o", (torch.float32,), n_req * pool.n_heads * pool.d_v)
     _check(_lib.sq_readout(pool.handle, _ptr(slot_ids), n_req, _ptr(q), _dtype_code(q), _ptr(o),
                            _stream(stream)), "sq_readout")

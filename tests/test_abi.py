@@ -110,3 +110,56 @@ def test_header_compiles_as_plain_c(tmp_path):
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
                         f"-I{os.path.join(ROOT, 'include')}", str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+class _FakePool:
+    """Shape-only stand-in: the binding's argument checks run before the
+    library sees the handle, so a CPU test never reaches a HIP call.  The
+    tensors live on torch's "meta" device, admitted for these tests only."""
+    handle, n_heads, d_k, d_v = None, 3, 8, 12
+
+
+@pytest.mark.parametrize("bad, err", [
+    (dict(q="cpu"), "not on a GPU"),
+    (dict(alpha="f64"), "alpha must be"),
+    (dict(beta="short"), "beta has"),
+    (dict(slot_ids="i64"), "slot_ids must be"),
+    (dict(o="bf16"), "o must be"),
+    (dict(v="strided"), "v is not contiguous"),
+    (dict(k="f16"), "share one dtype"),
+])
+def test_binding_checks_tensor_arguments(sq, bad, err, monkeypatch):
+    import torch
+    monkeypatch.setattr(sq, "_DEVICE_TYPES", ("cuda", "meta"))
+    p, n = _FakePool, 2
+    meta = torch.device("meta")
+    args = dict(slot_ids=torch.zeros(n, dtype=torch.int32, device=meta),
+                q=torch.zeros(n, p.n_heads, p.d_k, device=meta),
+                k=torch.zeros(n, p.n_heads, p.d_k, device=meta),
+                v=torch.zeros(n, p.n_heads, p.d_v, device=meta),
+                alpha=torch.zeros(n, p.n_heads, device=meta),
+                beta=torch.zeros(n, p.n_heads, device=meta),
+                o=torch.zeros(n, p.n_heads, p.d_v, device=meta))
+    which, how = next(iter(bad.items()))
+    x = args[which]
+    args[which] = {"cpu": lambda: torch.zeros(x.shape, dtype=x.dtype),
+                   "f64": lambda: x.double(),
+                   "short": lambda: x[:1],
+                   "i64": lambda: x.long(),
+                   "bf16": lambda: x.bfloat16(),
+                   "strided": lambda: torch.zeros(n, p.n_heads, 2 * p.d_v, device=meta)[..., ::2],
+                   "f16": lambda: x.half()}[how]()
+    with pytest.raises((sq.SqError, TypeError), match=err):
+        sq.sq_decode_step(p, **args)
+
+
+def test_binding_checks_per_channel_gate_shape(sq, monkeypatch):
+    import torch
+    monkeypatch.setattr(sq, "_DEVICE_TYPES", ("cuda", "meta"))
+    p, n, meta = _FakePool, 2, torch.device("meta")
+    q = torch.zeros(n, p.n_heads, p.d_k, device=meta)
+    v = torch.zeros(n, p.n_heads, p.d_v, device=meta)
+    ids = torch.zeros(n, dtype=torch.int32, device=meta)
+    beta = torch.zeros(n, p.n_heads, device=meta)
+    with pytest.raises(sq.SqError, match="alpha has 6 elements, expected 48"):
+        sq.sq_decode_step_kda(p, ids, q, q, v, torch.zeros(n, p.n_heads, device=meta), beta)

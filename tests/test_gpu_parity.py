@@ -214,8 +214,13 @@ def test_host_errors_with_a_live_pool(sq, orc):
     si = I.step_inputs(w, 0)
     q, k, v = si.q.cuda(), si.k.cuda(), si.v.cuda()
     a, b = si.alpha.cuda(), si.beta.cuda()
-    with pytest.raises(sq.SqError) as e:
+    with pytest.raises(sq.SqError) as e:  # the library's own check: more requests than slots
         too_many = torch.zeros(3, dtype=torch.int32, device="cuda")
+        sq._check(sq._lib.sq_decode_step(case.pool.handle, too_many.data_ptr(), 3, q.data_ptr(),
+                                         k.data_ptr(), v.data_ptr(), 1, a.data_ptr(), b.data_ptr(),
+                                         None, None), "too many requests")
+    assert e.value.status == sq.SQ_ERR_INVALID
+    with pytest.raises(sq.SqError) as e:  # the binding's: q sized for 2 requests, 3 slot ids
         sq.sq_decode_step(case.pool, too_many, q, k, v, a, b)
     assert e.value.status == sq.SQ_ERR_INVALID
     with pytest.raises(sq.SqError):
