@@ -55,6 +55,9 @@
  *     as void*, NULL = the null stream); no call synchronizes.  Results are
  *     visible after the caller synchronizes that stream.  Calls that touch the
  *     same pool must be ordered on one stream.
+ *   - A pool lives on the device that was current at sq_pool_alloc.  Calls
+ *     that enqueue work on it must be made with that device current (else
+ *     SQ_ERR_INVALID, nothing enqueued); sq_pool_free switches to it itself.
  *   - A slot must not appear twice in one slot_ids batch: two workgroups would
  *     update the same tile (undefined result).  The step does not check slot
  *     ids on the device; sq_check_slots does, as a separate call.

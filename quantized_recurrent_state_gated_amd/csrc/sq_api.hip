@@ -183,7 +183,14 @@ static int pool_alloc(const sq_pool_desc *desc, sq_pool **out)
 void sq_pool_free(sq_pool *pool)
 {
     if (!pool) return;
-    if (pool->dtab) (void)hipFree(pool->dtab);
+    if (pool->dtab) {
+        // free on the pool's own device, then restore the caller's
+        int cur = -1;
+        const bool switched = hipGetDevice(&cur) == hipSuccess && cur != pool->device &&
+                              hipSetDevice(pool->device) == hipSuccess;
+        (void)hipFree(pool->dtab);
+        if (switched) (void)hipSetDevice(cur);
+    }
     delete pool;
 }
 
@@ -214,9 +221,19 @@ static sqk::StepArgs base_args(const sq_pool *p, const int32_t *slot_ids)
     return a;
 }
 
+// Work is launched on the current device; the pool's buffers live on the
+// device that was current at sq_pool_alloc.
+static int check_device(const sq_pool *p)
+{
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SQ_ERR_HIP;
+    return cur == p->device ? SQ_OK : SQ_ERR_INVALID;
+}
+
 static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16, int32_t n_req,
                        void *stream)
 {
+    if (int st = check_device(p)) return st;
     // every launch must fit a 1-D grid of at most 2^31 - 1 workgroups: one per
     // tile for the step and readout, one per 256 blocks for store and load
     const uint64_t tiles = (uint64_t)n_req * (uint64_t)p->n_heads;
@@ -343,6 +360,7 @@ int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_
 {
     if (!pool || !result || n_req < 0 || (n_req > 0 && !slot_ids) || !aligned(result, 4))
         return SQ_ERR_INVALID;
+    if (int st = check_device(pool)) return st;
     if (sqk::launch_check_slots(slot_ids, n_req, pool->n_slots, pool->d_stamps, result,
                                 (hipStream_t)stream) != hipSuccess)
         return SQ_ERR_HIP;

@@ -91,7 +91,7 @@ def test_d128_every_width(sq, orc, qkv):
     run_teacher_forced(Case(sq, orc, w, n_slots=5, slots=[4, 1, 2]), w.steps, f"mix-{qkv}")
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (12, 20), (128, 64), (64, 128), (256, 32), (4, 4)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (12, 20), (128, 64), (64, 128), (256, 32), (4, 4), (256, 256)])
 def test_other_shapes(sq, orc, dk, dv):
     w = I.Workload("shape", 2, 6, dk, dv, 3, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1}, seed=dk * 1000 + dv)
     run_teacher_forced(Case(sq, orc, w), w.steps, f"shape{dk}x{dv}")
