@@ -29,7 +29,11 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized state-update heads·tokens/s + achieved HBM GB/s (70 req × 2304 heads)"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "quantized_recurrent_state_gated_amd", "csrc", "sq_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step128_serving.json")
+
+
+def traffic_file(workload: str) -> str:
+    """Counter-measured HBM bytes of the step launches of one workload."""
+    return os.path.join(ROOT, "profiles", f"traffic_step128_{workload}.json")
 
 
 def log(*a):
@@ -57,15 +61,16 @@ STEP_KERNEL = "k_step128<unsigned short, true, false, 128, 5>"
 KDA_KERNEL = "k_step128<unsigned short, true, true, 128, 5>"
 
 
-def traffic_from_profile(sha: str, which: str = "step"):
+def traffic_from_profile(sha: str, workload: str, which: str = "step"):
     """HBM bytes per launch measured by rocprofv3 counters for this exact kernel
-    source, scaled by the copy-kernel calibration; None if absent or stale."""
+    source and workload, scaled by the copy-kernel calibration; None if absent
+    or stale."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != sha or which not in t:
+    if t.get("kernel_source_sha") != sha or t.get("workload") != workload or which not in t:
         return None
     return t[which].get("hbm_bytes_per_launch")
 
@@ -84,7 +89,7 @@ def _pmc_rows(path, counter):
     return step, kda, copies
 
 
-def pmc_summary(fetch_csv: str, write_csv: str) -> int:
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> int:
     """HBM bytes per step launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by the factor that makes the same counter read the known size
     of the 1 GiB calibration copy."""
@@ -102,18 +107,21 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> int:
                 "raw_fetch_kib": statistics.median(f) / 1024,
                 "raw_write_kib": statistics.median(w) / 1024}
 
-    out = {"kernel_source_sha": kernel_source_sha(), "step": one(STEP_KERNEL, fs, ws),
+    wl = "" if workload == "serving" else f" --workload {workload}"
+    out = {"kernel_source_sha": kernel_source_sha(), "workload": workload,
+           "step": one(STEP_KERNEL, fs, ws),
            "fetch_factor": ff, "write_factor": fw,
            "calibration": "1 GiB device copy (hipMemcpy D2D blit kernel): FETCH_SIZE and WRITE_SIZE "
                           "each scaled so that it reads 1 GiB",
            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o <name> -- python3 "
                         f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp32-baseline "
-                        f"--no-copy-ceiling --copy-calibration"
+                        f"--no-copy-ceiling --copy-calibration{wl}"
                         for c in ("FETCH_SIZE", "WRITE_SIZE")]}
     if fk and wk:
         out["channel_gate_step"] = one(KDA_KERNEL, fk, wk)
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    path = traffic_file(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
     return 0
@@ -205,7 +213,7 @@ def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, 
     byts = algorithmic_bytes_per_step(w, bits) + w.n_req * w.n_heads * 4 * (w.dk - 1)
     gbps = byts / (ms / 1e3) / 1e9
     return {"value": w.n_req * w.n_heads / (ms / 1e3), "unit": "heads*tokens/s",
-            "traffic": traffic_from_profile(kernel_source_sha(), "channel_gate_step"),
+            "traffic": traffic_from_profile(kernel_source_sha(), w.name, "channel_gate_step"),
             "ms_per_step": ms, "hbm_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": byts, "time_vs_scalar_gate_step": ms / quant_ms,
             "kernel": "k_step128 per-channel-gate instance"}
@@ -387,7 +395,7 @@ def main() -> int:
                     help="print the step kernel's row of a rocprofv3 --stats csv and exit")
     args = ap.parse_args()
     if args.pmc_summary:
-        return pmc_summary(*args.pmc_summary)
+        return pmc_summary(*args.pmc_summary, args.workload)
     if args.trace_summary:
         return trace_summary(args.trace_summary)
 
@@ -470,7 +478,7 @@ def main() -> int:
     bpstep = algorithmic_bytes_per_step(w, bits)
     gbps = bpstep / (ms_per_step / 1e3) / 1e9
     sha = kernel_source_sha()
-    traffic = traffic_from_profile(sha)
+    traffic = traffic_from_profile(sha, w.name)
     stats = I.pool_stats(w)
     result = {
         "metric": METRIC,

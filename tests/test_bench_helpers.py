@@ -34,19 +34,22 @@ def test_pmc_summary_scales_by_the_copy_and_picks_exact_kernels(tmp_path, monkey
     _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE",
              [(copy, 2), (copy, gib), (step, 2000), (step, 2000), (kda, 2000), (f32, 9e9),
               (conv, 5e9)])
-    out = tmp_path / "traffic.json"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    assert bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv")) == 0
-    t = json.load(open(out))
+    monkeypatch.setattr(bench, "traffic_file", lambda wl: str(tmp_path / f"traffic_{wl}.json"))
+    assert bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "highconc") == 0
+    t = json.load(open(tmp_path / "traffic_highconc.json"))
+    assert t["workload"] == "highconc"
+    assert all(c.endswith("--copy-calibration --workload highconc") for c in t["commands"])
     assert t["fetch_factor"] == 2.0 and t["write_factor"] == 1.0
     assert t["step"]["fetch_bytes_per_launch"] == 2.0 * 1000 * 1024  # median, scaled
     assert t["step"]["write_bytes_per_launch"] == 2000 * 1024
     assert t["step"]["dispatches"] == [3, 2]
     assert t["channel_gate_step"]["hbm_bytes_per_launch"] == (2.0 * 1100 + 2000) * 1024
-    # the profile is used only for the kernel source it was taken on
-    assert bench.traffic_from_profile(t["kernel_source_sha"]) == t["step"]["hbm_bytes_per_launch"]
-    assert bench.traffic_from_profile("0" * 16) is None
-    assert bench.traffic_from_profile(t["kernel_source_sha"], "channel_gate_step") is not None
+    # the profile is used only for the kernel source and the workload it was taken on
+    sha = t["kernel_source_sha"]
+    assert bench.traffic_from_profile(sha, "highconc") == t["step"]["hbm_bytes_per_launch"]
+    assert bench.traffic_from_profile("0" * 16, "highconc") is None
+    assert bench.traffic_from_profile(sha, "serving") is None
+    assert bench.traffic_from_profile(sha, "highconc", "channel_gate_step") is not None
 
 
 class _FakeSq:
