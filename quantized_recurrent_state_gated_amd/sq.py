@@ -178,6 +178,10 @@ def sq_pool_alloc(n_slots: int, n_heads: int, d_k: int, d_v: int, head_bits, row
                   col_scale, state, state_bytes: int | None = None) -> SqPool:
     """Wrap sq_pool_alloc; `state` is a uint8 device tensor (the caller's buffer)."""
     arr, nb = _bits_array(head_bits)
+    _arg(row_scale, "sq_pool_alloc", "row_scale", (torch.float32,), n_heads * d_k)
+    _arg(col_scale, "sq_pool_alloc", "col_scale", (torch.float32,), n_heads * d_v)
+    if isinstance(state, torch.Tensor):
+        _arg(state, "sq_pool_alloc", "state", (state.dtype,), state.numel())
     if state_bytes is None:
         state_bytes = state.numel() * state.element_size() if hasattr(state, "numel") else 0
     desc = SqPoolDesc(n_slots, n_heads, d_k, d_v, arr, _ptr(row_scale), _ptr(col_scale),

@@ -163,3 +163,17 @@ def test_binding_checks_per_channel_gate_shape(sq, monkeypatch):
     beta = torch.zeros(n, p.n_heads, device=meta)
     with pytest.raises(sq.SqError, match="alpha has 6 elements, expected 48"):
         sq.sq_decode_step_kda(p, ids, q, q, v, torch.zeros(n, p.n_heads, device=meta), beta)
+
+
+def test_binding_checks_pool_alloc_scales(sq, monkeypatch):
+    import torch
+    monkeypatch.setattr(sq, "_DEVICE_TYPES", ("cuda", "meta"))
+    meta = torch.device("meta")
+    state = torch.empty(1 << 16, dtype=torch.uint8, device=meta)
+    r = torch.ones(2, 16, device=meta)
+    with pytest.raises(TypeError, match="row_scale must be"):
+        sq.sq_pool_alloc(2, 2, 16, 16, [8, 4], r.double(), r, state)
+    with pytest.raises(sq.SqError, match="col_scale has 16 elements, expected 32"):
+        sq.sq_pool_alloc(2, 2, 16, 16, [8, 4], r, r[0], state)
+    with pytest.raises(sq.SqError, match="row_scale is not on a GPU"):
+        sq.sq_pool_alloc(2, 2, 16, 16, [8, 4], torch.ones(2, 16), r, state)
