@@ -329,19 +329,13 @@ __host__ __forceinline__ uint32_t xcd_grid(uint32_t n_req, uint32_t H)
 // ---------------------------------------------------------------- d = 128 step
 //
 // Shared memory of one tile.  Two bodies use it: tile128 (the fused launch
-// over 4/6/8-bit and FP16 tiles, 128 threads, codes held as packed halves;
-// below) and tile128_wide (FP32-state tiles, 256 threads, fp32 registers).
-//
-// tile128_wide: one 256-thread workgroup per tile.  Thread t owns column
-// block cb = t % 32 (columns 4cb..4cb+3) and row group rg = t / 32, i.e. the
-// four 4x4 blocks in block rows rg, rg+8, rg+16, rg+24 (16 rows).  For a
-// fixed m the 64 lanes of a wave read 64 consecutive blocks, so every load
-// and store instruction of a wave covers one contiguous span.  Partial column
-// sums over a thread's 16 rows are combined across the 8 row groups through
-// LDS.
+// over 4/6/8-bit and FP16 tiles, codes held as packed halves; below) and
+// tile128_wide (FP32- and BF16-state tiles, 256 threads).
 
 struct Smem128 {
-    float w[128], g[128], a[128];  // per-row factors k_i r_i, q_i r_i, beta k_i / r_i
+    alignas(16) float w[128];      // per-row factors k_i r_i (wide tiles: k_i)
+    alignas(16) float g[128];      // q_i r_i (wide tiles: q_i)
+    alignas(16) float a[128];      // beta k_i / r_i (wide tiles: beta k_i)
     alignas(16) float4 wg[128];    // per-row {w 2^-s0, w 2^-s1, g 2^-s0, g 2^-s1} (half codes)
     alignas(16) float red[8][2][128];  // [row group][u, y][column] partial sums
     alignas(16) float b[128];      // per-column (v_j - alpha u_j) / c_j
@@ -355,22 +349,39 @@ struct Smem128K : Smem128 {
     alignas(16) float4 pa[128];
 };
 
-template <int BITS, typename T, bool UPDATE, bool CHG, typename SM>
+// tile128_wide: an unquantized FP32 or BF16 state, one 256-thread workgroup
+// per tile.  Every load and store instruction of a wave moves one contiguous
+// kilobyte: lane l takes the l-th 16-byte chunk of its span.  A 16-byte chunk
+// of an FP32 block is one column's four rows, of a BF16 block two columns'
+// four rows, so a lane owns CPL = 1 or 2 columns and four rows of every block
+// row it visits:
+//   FP32: a block row is 2 KB; wave w takes the half ch = w % 2 (columns
+//         64 ch + lane) of block rows 16 (w / 2) .. 16 (w / 2) + 15;
+//   BF16: a block row is 1 KB; wave w takes block rows 8 w .. 8 w + 7
+//         (columns 2 lane and 2 lane + 1).
+// A lane's column sums over its 64 rows stay in registers; the two (FP32) or
+// four (BF16) row groups are combined through LDS.
+
+// threads per wide tile (measured at 70 x 2304: FP32 states 3.88 ms per step
+// with 256, 3.88 with 128, 3.94 with 512; BF16 1.93-1.96 ms for all three)
+constexpr int kWideTPB = 256;
+
+template <int FMT, typename T, bool UPDATE, bool CHG, typename SM>
 __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM &sm)
 {
-    constexpr int W = fw<BITS>() / 2;
-    constexpr bool QUANT = BITS <= 8;
-    constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
-    constexpr int BLK_BYTES = 2 * fw<BITS>();
-    // code tiles stream with the nontemporal hint (measured faster on gfx950);
-    // FP16/FP32 tiles measured faster without it
-    constexpr bool NT = QUANT;
+    static_assert(FMT == 32 || FMT == kBF16, "unquantized states only");
+    constexpr int E = FMT == 32 ? 4 : 2;        // bytes per element
+    constexpr int CPL = 4 / E;                  // columns per lane
+    constexpr int NCH = 128 / (64 * CPL);       // column spans: 2 (FP32) or 1 (BF16)
+    constexpr int NRG = kWideTPB / 64 / NCH;    // row groups
+    constexpr int NI = 32 / NRG;                // block rows per wave
+    static_assert(NRG >= 1 && NRG <= 8 && 32 % NRG == 0, "row groups");
+    constexpr int ROW_BYTES = 32 * 16 * E;      // one block row: 2048 or 1024 bytes
 
-    const int t = threadIdx.x;
-    const int cb = t & 31, rg = t >> 5;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int ch = wv % NCH, rgp = wv / NCH;
     const long nh = (long)n * a.H + h;
-    const int slot = a.slot_ids[n];
-    uint8_t *tile = a.pool + (uint64_t)slot * a.slab + (uint64_t)a.head_off[h];
+    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
     const T *q = reinterpret_cast<const T *>(a.q);
     const T *k = reinterpret_cast<const T *>(a.k);
     const T *v = reinterpret_cast<const T *>(a.v);
@@ -386,108 +397,124 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
     const int tr = t & 127;
     const float qi = ld1(q, nh * 128 + tr);
     const float ki = UPDATE ? ld1(k, nh * 128 + tr) : 0.0f;
-    const float rs = QUANT ? a.rsc[(long)h * 128 + tr] : 1.0f;
     const float gate = CHG ? a.alpha[nh * 128 + tr] : 1.0f;
     const float vj = UPDATE ? ld1(v, nh * 128 + tr) : 0.0f;
-    const float cjs = QUANT ? a.csc[(long)h * 128 + tr] : 1.0f;
 
-    // the tile: 4 blocks per thread
-    uint32_t d[4][W];
+    // the lane's chunks: block rows rgp NI + m, m = 0 .. NI - 1
+    uint8_t *span = tile + (long)(rgp * NI) * ROW_BYTES + 1024 * ch + 16 * lane;
+    uint32_t d[NI][4];
 #pragma unroll
-    for (int m = 0; m < 4; m++) load_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, d[m]);
+    for (int m = 0; m < NI; m++) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(span + (long)m * ROW_BYTES);
+        d[m][0] = x.x; d[m][1] = x.y; d[m][2] = x.z; d[m][3] = x.w;
+    }
 
-    // per-row factors and the three tile sums (waves 0 and 1 hold rows 0..127;
-    // waves 2 and 3 write the same values again)
     {
-        const float wi = ki * rs * gate, gi = qi * rs * gate;
-        sm.w[tr] = wi;
-        sm.g[tr] = gi;
-        const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(rs) : beta * ki;
-        if constexpr (CHG) sm.pa[tr] = make_float4(ai, gate, gate, OFF * (1.0f - gate));
-        else if (UPDATE) sm.a[tr] = ai;
-        sm.vc[tr] = make_float2(vj, cjs);
-        const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
-        if (t < 128 && (t & 63) == 0) {
-            sm.sum[t >> 6][0] = s0;
-            sm.sum[t >> 6][1] = s1;
-            sm.sum[t >> 6][2] = s2;
-        }
+        sm.w[tr] = ki * gate;
+        sm.g[tr] = qi * gate;
+        if constexpr (CHG) sm.pa[tr] = make_float4(beta * ki, gate, 0.0f, 0.0f);
+        else if (UPDATE) sm.a[tr] = beta * ki;
+        sm.vc[tr] = make_float2(vj, 1.0f);
+        const float s0 = wave_sum(qi * ki);
+        if (t < 128 && (t & 63) == 0) sm.sum[t >> 6][0] = s0;
     }
     __syncthreads();
 
-    // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
-    float f[4][16];
-#pragma unroll
-    for (int m = 0; m < 4; m++) decode<BITS>(d[m], f[m]);
-    float pu[4] = {0, 0, 0, 0}, py[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const int i0 = 4 * (rg + 8 * m);
-#pragma unroll
-        for (int ri = 0; ri < 4; ri++) {
-            const float w = sm.w[i0 + ri], g = sm.g[i0 + ri];
-#pragma unroll
-            for (int cj = 0; cj < 4; cj++) {
-                if (UPDATE) pu[cj] = fmaf(w, f[m][4 * cj + ri], pu[cj]);
-                py[cj] = fmaf(g, f[m][4 * cj + ri], py[cj]);
-            }
+    // element (row r of the chunk, lane column c) of chunk m
+    auto elem = [&](int m, int r, int c) -> float {
+        if constexpr (FMT == 32) {
+            return __uint_as_float(d[m][r]);
+        } else {
+            // dword 2c + (r >> 1) holds rows (r & ~1, r | 1) of lane column c
+            const uint32_t x = d[m][2 * c + (r >> 1)];
+            return __uint_as_float((r & 1) ? (x & 0xffff0000u) : (x << 16));
         }
+    };
+
+    // pass 1: this lane's column sums over its 64 rows
+    float pu[CPL], py[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) pu[c] = py[c] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NI; m++) {
+        const int i0 = 4 * (rgp * NI + m);
+        const float4 w4 = *reinterpret_cast<const float4 *>(&sm.w[i0]);
+        const float4 g4 = *reinterpret_cast<const float4 *>(&sm.g[i0]);
+        const float wr[4] = {w4.x, w4.y, w4.z, w4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                const float x = elem(m, r, c);
+                if (UPDATE) pu[c] = fmaf(wr[r], x, pu[c]);
+                py[c] = fmaf(gr[r], x, py[c]);
+            }
     }
-    *reinterpret_cast<float4 *>(&sm.red[rg][0][4 * cb]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
-    *reinterpret_cast<float4 *>(&sm.red[rg][1][4 * cb]) = make_float4(py[0], py[1], py[2], py[3]);
+    const int j0 = CPL * (64 * ch + lane);  // the lane's first column
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+        sm.red[rgp][0][j0 + c] = pu[c];
+        sm.red[rgp][1][j0 + c] = py[c];
+    }
     __syncthreads();
 
     // column finalisation: thread j < 128 owns column j
     if (t < 128) {
         float U = 0.0f, Y = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 8; r++) {
+        for (int r = 0; r < NRG; r++) {
             U += sm.red[r][0][t];
             Y += sm.red[r][1][t];
         }
         const float qk = sm.sum[0][0] + sm.sum[1][0];
-        const float Wsum = sm.sum[0][1] + sm.sum[1][1];
-        const float Gsum = sm.sum[0][2] + sm.sum[1][2];
-        const float2 vc = sm.vc[t];
-        const float cj = vc.y;
-        const float uj = cj * (U - OFF * Wsum);
-        const float yj = cj * (Y - OFF * Gsum);
         if (!UPDATE) {
-            a.o[nh * 128 + t] = yj;
+            a.o[nh * 128 + t] = Y;
         } else {
-            const float e = vc.x - alpha * uj;
-            if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * qk * e);
-            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cj) : e;
+            const float e = sm.vc[t].x - alpha * U;
+            if (a.o) a.o[nh * 128 + t] = fmaf(alpha, Y, beta * qk * e);
+            sm.b[t] = e;
         }
     }
     if (!UPDATE) return;
     __syncthreads();
-    const float4 b4 = *reinterpret_cast<const float4 *>(&sm.b[4 * cb]);
-    const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+    float b[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) b[c] = sm.b[j0 + c];
 
-    // pass 2: z = alpha n + a_i b_j + OFF (1 - alpha), requantize, repack, store
-    const float C = OFF * (1.0f - alpha);
+    // pass 2: S' = gate S + a_i b_j, rounded to the storage format, stored in place
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const int i0 = 4 * (rg + 8 * m);
-        float z[16];
+    for (int m = 0; m < NI; m++) {
+        const int i0 = 4 * (rgp * NI + m);
+        float z[4][CPL];
 #pragma unroll
-        for (int ri = 0; ri < 4; ri++) {
+        for (int r = 0; r < 4; r++) {
+            float ai, gi;
             if constexpr (CHG) {
-                const float4 p = sm.pa[i0 + ri];
-#pragma unroll
-                for (int cj = 0; cj < 4; cj++)
-                    z[4 * cj + ri] = fmaf(p.y, f[m][4 * cj + ri], fmaf(p.x, b[cj], p.w));
+                const float4 p = sm.pa[i0 + r];
+                ai = p.x;
+                gi = p.y;
             } else {
-                const float ai = sm.a[i0 + ri];
-#pragma unroll
-                for (int cj = 0; cj < 4; cj++)
-                    z[4 * cj + ri] = fmaf(alpha, f[m][4 * cj + ri], fmaf(ai, b[cj], C));
+                ai = sm.a[i0 + r];
+                gi = alpha;
             }
+#pragma unroll
+            for (int c = 0; c < CPL; c++) z[r][c] = fmaf(gi, elem(m, r, c), ai * b[c]);
         }
-        uint32_t dn[W];
-        encode<BITS>(z, dn);
-        store_block<BITS, NT>(tile + (long)((rg + 8 * m) * 32 + cb) * BLK_BYTES, dn);
+        uint32_t o4[4];
+        if constexpr (FMT == 32) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) o4[r] = __float_as_uint(z[r][0]);
+        } else {
+            // round half to even, two values per conversion (v_cvt_pk_bf16_f32)
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+                for (int p = 0; p < 2; p++) {
+                    const f32x2 x = {z[2 * p][c], z[2 * p + 1][c]};
+                    o4[2 * c + p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+                }
+        }
+        *reinterpret_cast<u32x4 *>(span + (long)m * ROW_BYTES) = u32x4{o4[0], o4[1], o4[2], o4[3]};
     }
 }
 
@@ -770,7 +797,7 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) v
 }
 
 template <int FMT, typename T, bool UPDATE, bool CHG>
-__global__ __launch_bounds__(256) void k_step128_wide(StepArgs a)
+__global__ __launch_bounds__(kWideTPB) void k_step128_wide(StepArgs a)
 {
     // FP32- or BF16-state heads of a d = 128 pool (a.heads / a.Hc)
     using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
@@ -1021,11 +1048,11 @@ template <int FMT, typename T>
 static void wide128_t(Op op, const StepArgs &a, dim3 grid, hipStream_t st)
 {
     if (op == OP_STEP)
-        hipLaunchKernelGGL((k_step128_wide<FMT, T, true, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_step128_wide<FMT, T, true, false>), grid, dim3(kWideTPB), 0, st, a);
     else if (op == OP_STEP_KDA)
-        hipLaunchKernelGGL((k_step128_wide<FMT, T, true, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_step128_wide<FMT, T, true, true>), grid, dim3(kWideTPB), 0, st, a);
     else
-        hipLaunchKernelGGL((k_step128_wide<FMT, T, false, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_step128_wide<FMT, T, false, false>), grid, dim3(kWideTPB), 0, st, a);
 }
 
 hipError_t launch_wide128(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_req,
