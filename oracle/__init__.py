@@ -24,7 +24,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# tests/test_oracle_mutants.py points child test runs at deliberately broken
+# builds through SQ_ORACLE_LIB; nothing else sets it
+_LIB_PATH = os.environ.get("SQ_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _u8p = ctypes.POINTER(ctypes.c_uint8)

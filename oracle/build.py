@@ -11,14 +11,14 @@ SRC = os.path.join(HERE, "sq_oracle.c")
 OUT = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = SRC, out: str = OUT) -> str:
     cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
-           "-D_GNU_SOURCE", "-Wall", "-Wextra", "-o", OUT + ".tmp", SRC, "-lm"]
+           "-D_GNU_SOURCE", "-Wall", "-Wextra", "-o", out + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(OUT + ".tmp", OUT)
-    return OUT
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
