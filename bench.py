@@ -401,8 +401,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the step shards by request slot or by "
-              "head with no exchange; multi-GPU runs are not part of it)", file=sys.stderr)
+        print("bench.py: the step is measured on one GPU only (--gpus 1); it would shard by request "
+              "slot or by head with no exchange, and multi-GPU runs are not implemented",
+              file=sys.stderr)
         return 2
 
     import numpy as np
