@@ -140,3 +140,40 @@ def test_drift_full_length(sq, orc):
 def test_serving_full_size_channel_gate(sq, orc):
     """The per-key-channel-gate step at the serving size, in the launch bench.py times."""
     run_fullsize(sq, orc, "serving", check_steps=(0, 1, 31), kda=True)
+
+
+def test_highconc_full_size_channel_gate(sq, orc):
+    """The per-key-channel-gate step at 256 x 2304 heads (88 % 4-bit)."""
+    run_fullsize(sq, orc, "highconc", check_steps=(0, 1, 15), kda=True)
+
+
+def test_serving_readout_full_size(sq, orc):
+    """sq_readout over the whole serving pool after two steps: o = S^T q from
+    the stored state, on sampled tiles of every width; the pool is unchanged."""
+    w = I.WORKLOADS["serving"]
+    say(f"[serving readout] init {w.n_req} x {w.n_heads}")
+    dp = DevicePool(sq, w)
+    for t in range(2):
+        si = I.step_inputs(w, t, "cuda")
+        sq.sq_decode_step(dp.pool, dp.slots, si.q, si.k, si.v, si.alpha, si.beta, None)
+    si = I.step_inputs(w, 2, "cuda")
+    rng = np.random.default_rng(11)
+    tiles = sample(w, dp.bits, rng, 2048)
+    before = dp.tile_bytes(tiles)
+    o = torch.empty(w.n_req, w.n_heads, w.dv, device="cuda")
+    sq.sq_readout(dp.pool, dp.slots, si.q, o)
+    torch.cuda.synchronize()
+    after = dp.tile_bytes(tiles)
+    assert all(np.array_equal(a, b) for a, b in zip(before, after)), "readout wrote the pool"
+    q, o_gpu = host_f32(si.q), o.cpu().numpy()
+
+    def one(i):
+        n, h = tiles[i]
+        return orc.readout_tile(int(dp.bits[h]), w.dk, w.dv, before[i], dp.rh[h], dp.ch[h], q[n, h])
+
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        ref = list(ex.map(one, range(len(tiles))))
+    tally = Tally()
+    tally.add_o(np.stack([o_gpu[n, h] for n, h in tiles]), np.stack(ref))
+    say(f"[serving readout] {len(tiles)} tiles: {tally.summary()}")
+    assert tally.o_worst <= 1.0, tally.summary()
