@@ -367,7 +367,8 @@ def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=256,
+                    help="timed steps (enough that the warm-up launches are a small part of a kernel trace)")
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first: after an idle spell launch times jump and take "
                          "~25-30 launches to settle")
