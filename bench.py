@@ -336,32 +336,39 @@ def cpu_model() -> str:
 
 def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
     """The oracle, as it stands, on a bounded sample: whole requests (all 2304
-    heads) of the same workload, calibrated to about target_s seconds."""
+    heads) of the same workload, calibrated to about target_s seconds on
+    n_threads threads; then one thread on 1/n_threads of that sample."""
     import numpy as np
     import oracle
 
-    off, slab = oracle.pool_layout(bits, w.dk, w.dv)
     q = si.q.float().cpu().numpy()
     k = si.k.float().cpu().numpy()
     v = si.v.float().cpu().numpy()
     al = si.alpha.cpu().numpy()
     be = si.beta.cpu().numpy()
 
-    def run(n):
+    def run(n, threads):
         slots = np.arange(n, dtype=np.int32)
         pool = get_pool(n)
         t0 = time.perf_counter()
         oracle.step_pool(pool, bits, w.dk, w.dv, r, c, slots, q[:n], k[:n], v[:n], al[:n], be[:n],
-                         n_threads=n_threads)
+                         n_threads=threads)
         return time.perf_counter() - t0
 
-    t1 = run(1)
+    t1 = run(1, n_threads)
     n = max(1, min(w.n_req, int(target_s / max(t1, 1e-3))))
-    tn = run(n) if n > 1 else t1
-    return {"value": n * w.n_heads / tn, "unit": "heads*tokens/s", "cores": n_threads,
-            "kind": "oracle", "cpu": cpu_model(),
-            "sample": f"{n} of {w.n_req} requests x all {w.n_heads} heads, one decode step "
-                      f"({n * w.n_heads} tiles, {tn:.1f} s wall on {n_threads} threads)"}
+    tn = run(n, n_threads) if n > 1 else t1
+    out = {"value": n * w.n_heads / tn, "unit": "heads*tokens/s", "cores": n_threads,
+           "kind": "oracle", "cpu": cpu_model(),
+           "sample": f"{n} of {w.n_req} requests x all {w.n_heads} heads, one decode step "
+                     f"({n * w.n_heads} tiles, {tn:.1f} s wall on {n_threads} threads)"}
+    if n_threads > 1:
+        n1 = max(1, n // n_threads)
+        t = run(n1, 1)
+        out["one_core"] = {"value": n1 * w.n_heads / t, "unit": "heads*tokens/s",
+                           "sample": f"{n1} of {w.n_req} requests x all {w.n_heads} heads "
+                                     f"({n1 * w.n_heads} tiles, {t:.1f} s on 1 thread)"}
+    return out
 
 
 def main() -> int:

@@ -88,3 +88,20 @@ def test_saturation_counts_codes_at_the_range_ends(orc):
     assert got.keys() == want.keys()
     for b in want:
         assert abs(got[b] - want[b]) < 1e-12, (b, got[b], want[b])
+
+
+def test_cpu_baseline_times_the_oracle_on_n_threads_and_one(orc):
+    from quantized_recurrent_state_gated_amd import inputs as I
+    w = I.scaled(I.WORKLOADS["layer"], 4, 6, 1)
+    bits = I.head_bits(w)
+    r, c = (x.numpy() for x in I.scales(w))
+    off, slab = orc.pool_layout(bits, w.dk, w.dv)
+    pool = np.zeros(w.n_req * slab, np.uint8)
+    S0 = torch.stack([I.initial_state(w, p) for p in range(w.n_req)]).numpy()
+    orc.store_pool(pool, bits, w.dk, w.dv, r, c, np.arange(w.n_req, dtype=np.int32), S0)
+    si = I.step_inputs(w, 0)
+    out = bench.cpu_baseline(w, bits, lambda n: pool[: n * slab].copy(), r, c, si, 2, 1e3)
+    assert out["kind"] == "oracle" and out["cores"] == 2 and out["value"] > 0
+    assert out["sample"].startswith(f"{w.n_req} of {w.n_req} requests")  # capped at the workload
+    assert out["one_core"]["value"] > 0
+    assert out["one_core"]["sample"].startswith(f"{w.n_req // 2} of {w.n_req} requests")
