@@ -36,8 +36,6 @@ knapsack in units of 2 bits).
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 import torch
 

@@ -5,7 +5,6 @@ import math
 import os
 
 import numpy as np
-import pytest
 import torch
 
 from quantized_recurrent_state_gated_amd import inputs as I
