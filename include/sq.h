@@ -131,7 +131,8 @@ int sq_pool_tile_offset(const sq_pool *pool, int32_t slot, int32_t head, uint64_
 /* Quantize-and-store: encode fp32 states S (DEVICE, [n_req][n_heads][d_k][d_v],
  * row-major) into the tiles of slots slot_ids[0..n_req) (DEVICE int32), with
  * the quantizer and layout above (the hand-off of a state computed elsewhere,
- * e.g. at prefill).  n_req == 0 is a no-op.  Asynchronous on `stream`. */
+ * e.g. at prefill).  n_req == 0 is a no-op.  Asynchronous on `stream`.
+ * Errors as for sq_decode_step (S must be 16-byte aligned). */
 int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const float *S,
                   void *stream);
 
@@ -141,7 +142,7 @@ int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const f
  * rounded once to fp32: fl32(q * fl32(r_i c_j)) for codes, the binary16 value
  * for pivots, the stored value for FP32 heads.  The pool is not modified.
  * n_req == 0 is a no-op.  Asynchronous on `stream`.  (Calibration,
- * checkpoint export, inspection.) */
+ * checkpoint export, inspection.)  Errors as for sq_pool_store. */
 int sq_pool_load(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, float *S,
                  void *stream);
 
@@ -153,7 +154,12 @@ int sq_pool_load(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, fl
  *   alpha, beta fp32 [n_req][n_heads] (gate in (0, 1], write strength in [0, 1]);
  *   o        fp32 [n_req][n_heads][d_v], written with S'^T q; may be NULL.
  * q/k/v/o must be 16-byte aligned.  The pool's tiles are updated in place.
- * n_req == 0 is a no-op.  Asynchronous on `stream`. */
+ * n_req == 0 is a no-op.  Asynchronous on `stream`.
+ * Errors: SQ_ERR_INVALID (null pool or required pointer, n_req < 0 or
+ * > n_slots, qkv_dtype not an sq_dtype, misaligned pointer, another device
+ * current), SQ_ERR_UNSUPPORTED (n_req * n_heads tiles exceed one launch
+ * grid), SQ_ERR_HIP (a launch failed).  Device data (slot values, alpha,
+ * beta, q/k/v) is not validated; see sq_check_slots for slot ids. */
 int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
                    const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
                    const float *beta, float *o, void *stream);
@@ -176,7 +182,8 @@ int sq_decode_step_kda(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, co
 /* Readout without update: o = S^T q from the stored state (dequantized), for
  * slots slot_ids[0..n_req).  q: DEVICE [n_req][n_heads][d_k] of q_dtype;
  * o: DEVICE fp32 [n_req][n_heads][d_v].  Does not modify the pool.  n_req == 0
- * is a no-op.  Asynchronous on `stream`. */
+ * is a no-op.  Asynchronous on `stream`.  Errors as for sq_decode_step (q and
+ * o required, 16-byte aligned). */
 int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
                int32_t q_dtype, float *o, void *stream);
 
