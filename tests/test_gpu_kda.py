@@ -114,3 +114,10 @@ def test_kda_mid_size_launch(sq, orc):
                    seed=52)
     assert 1024 <= w.n_req * w.n_heads < 16384
     run_teacher_forced(KdaCase(sq, orc, w), w.steps, "kda-mid")
+
+
+def test_kda_head_groups_of_unequal_size(sq, orc):
+    """The per-channel gate over 3 x 100 heads (XCD head groups of 12 and 13)."""
+    w = I.Workload("kh100", 3, 100, 128, 128, 2, {4: 30, 6: 30, 8: 30, 16: 4, 32: 3, I.BITS_BF16: 3},
+                   seed=100)
+    run_teacher_forced(KdaCase(sq, orc, w, n_slots=4, slots=[2, 0, 3]), w.steps, "kda-h100")

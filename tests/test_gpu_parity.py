@@ -376,3 +376,17 @@ def test_mid_size_launch_takes_256_threads(sq, orc):
                    {4: 96, 6: 196, 8: 96, 16: 4, 32: 4, I.BITS_BF16: 4}, seed=51)
     assert 1024 <= w.n_req * w.n_heads < 16384
     run_teacher_forced(Case(sq, orc, w, n_slots=6, slots=[5, 0, 3, 1]), w.steps, "mid")
+
+
+@pytest.mark.parametrize("n_req,H", [(3, 100), (8, 150)])
+def test_head_groups_of_unequal_size(sq, orc, n_req, H):
+    """Pools of 64 or more heads split the heads of every request into 8 XCD
+    groups; with H not a multiple of 8 the groups differ in size (12/13 and
+    18/19 heads) and the rounded-up grid has surplus workgroups.  Every tile
+    must still be stepped exactly once: 300 tiles (128-thread launch) and
+    1,200 tiles (256-thread launch), every width, scrambled slots."""
+    mix = {4: H // 4, 6: H // 4, 8: H // 4, 16: 2, 32: 2}
+    mix[I.BITS_BF16] = H - sum(mix.values())
+    w = I.Workload(f"h{H}", n_req, H, 128, 128, 2, mix, seed=H)
+    slots = list(range(n_req + 1))[::-1][:n_req]
+    run_teacher_forced(Case(sq, orc, w, n_slots=n_req + 1, slots=slots), w.steps, f"h{H}")
