@@ -390,3 +390,24 @@ def test_head_groups_of_unequal_size(sq, orc, n_req, H):
     w = I.Workload(f"h{H}", n_req, H, 128, 128, 2, mix, seed=H)
     slots = list(range(n_req + 1))[::-1][:n_req]
     run_teacher_forced(Case(sq, orc, w, n_slots=n_req + 1, slots=slots), w.steps, f"h{H}")
+
+
+@pytest.mark.parametrize("dk,dv", [(12, 20), (64, 128), (256, 32)])
+def test_readout_other_shapes(sq, orc, dk, dv):
+    """sq_readout through the any-shape kernel, every width: o = S^T q of the
+    stored state, the pool unchanged."""
+    w = I.Workload("ro", 3, 6, dk, dv, 1, {4: 1, 6: 1, 8: 1, 16: 1, 32: 1, I.BITS_BF16: 1},
+                   seed=dk * 7 + dv)
+    case = Case(sq, orc, w, n_slots=4, slots=[3, 0, 2])
+    case.step(I.step_inputs(w, 0))  # read a state that has been through a step
+    start = case.host()
+    si = I.step_inputs(w, 1)
+    o = torch.empty(w.n_req, w.n_heads, dv, device="cuda")
+    sq.sq_readout(case.pool, case.slots_d, si.q.cuda(), o)
+    torch.cuda.synchronize()
+    assert np.array_equal(case.host(), start)
+    o_ref = orc.readout_pool(start, case.bits, dk, dv, case.r, case.c, case.slots, host_f32(si.q))
+    t = Tally()
+    t.add_o(o.cpu().numpy(), o_ref)
+    say(f"[readout {dk}x{dv}] {t.summary()}")
+    t.check()
