@@ -61,8 +61,11 @@
  *   - A slot must not appear twice in one slot_ids batch: two workgroups would
  *     update the same tile (undefined result).  The step does not check slot
  *     ids on the device; sq_check_slots does, as a separate call.
- *   - Non-finite inputs (alpha, beta, q, k, v, scales) are a caller error; the
- *     resulting codes are unspecified but stay in the code range.
+ *   - Non-finite inputs (alpha, beta, q, k, v, scales) are a caller error.  The
+ *     result is defined on the updated value as the kernel evaluates it: a
+ *     NaN quotient S'/s becomes code 0, +-Inf the nearest bound +-Q; FP16,
+ *     BF16 and FP32 heads store the non-finite value.  Either way the pool's
+ *     sticky flag is set (sq_pool_last_device_error).
  *   - d_k and d_v must be multiples of 4 and at most 256; d_k = d_v = 128 takes
  *     the tuned kernels, other shapes a plain one.
  */
@@ -85,7 +88,8 @@ typedef enum {
     SQ_ERR_INVALID = -1,     /* null pointer, bad size, misaligned pointer, buffer too small */
     SQ_ERR_UNSUPPORTED = -2, /* head_bits not in {4,6,8,16,32,144}, or d_k/d_v not supported */
     SQ_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
-    SQ_ERR_NOMEM = -4        /* host or device allocation of the pool's tables failed */
+    SQ_ERR_NOMEM = -4,       /* host or device allocation of the pool's tables failed */
+    SQ_ERR_DEVICE = -5       /* sq_pool_last_device_error: a kernel met a non-finite value */
 } sq_status;
 
 typedef enum {
@@ -98,25 +102,37 @@ typedef struct {
     int32_t n_heads;          /* recurrent heads per request, >= 1 */
     int32_t d_k, d_v;         /* state rows (key dims) and columns (value dims) */
     const uint8_t *head_bits; /* HOST [n_heads], each in {4, 6, 8, 16, 32, 144}; copied */
-    const float *row_scale;   /* DEVICE [n_heads][d_k] fp32, r_i > 0; borrowed, read by
-                                 every call; entries of unquantized heads are ignored */
-    const float *col_scale;   /* DEVICE [n_heads][d_v] fp32, c_j > 0; as row_scale */
+    const float *row_scale;   /* DEVICE fp32, r_i > 0: [n_heads][d_k], or with a slot stride
+                                 S the factors of slot p, head h at row_scale + (p*S + h)*d_k;
+                                 borrowed, read by every call; entries of unquantized heads
+                                 are ignored */
+    const float *col_scale;   /* DEVICE fp32, c_j > 0: [n_heads][d_v], or at
+                                 col_scale + (p*S + h)*d_v; as row_scale */
+    int64_t scale_slot_stride;/* S: 0 = one set of factors per head, shared by every slot;
+                                 else S >= n_heads and every slot has its own factors
+                                 ([P5] 空间维度: each row and each column of a state matrix
+                                 has its own factor); the arrays then hold n_slots*S vectors */
     void *state;              /* DEVICE, 256-byte aligned, >= sq_pool_bytes(...) bytes,
                                  laid out as described above; borrowed */
     uint64_t state_bytes;     /* size of the state buffer in bytes */
 } sq_pool_desc;
 
-/* Bytes the state buffer needs for this shape: n_slots * slab_bytes.
+/* Bytes the state buffer needs for this shape: n_slots * slab_bytes.  One
+ * resident state per request slot ([P1] 背景; [P5] opening: the pool grows
+ * with concurrency), each head stored at its own width ([P5] 时间维度).
  * Returns 0 if any argument is invalid or unsupported.  Host only. */
 uint64_t sq_pool_bytes(int32_t n_slots, int32_t n_heads, int32_t d_k, int32_t d_v,
                        const uint8_t *head_bits);
 
 /* Validate desc, compute the tile offsets and upload them (and the per-width
- * head lists) to a small device table.  On success *out receives a handle to
+ * head lists) to a small device table: the per-request state pool ([P1] 背景;
+ * [P5] opening) with per-head widths and FP16 pivots ([P5] 时间维度) and
+ * row x column factors ([P5] 空间维度).  On success *out receives a handle to
  * release with sq_pool_free.  Errors: SQ_ERR_INVALID (null desc/out/pointers,
  * n_slots or n_heads < 1, state not 256-byte aligned, scales not 16-byte
- * aligned, state_bytes too small), SQ_ERR_UNSUPPORTED (bits, d_k, d_v),
- * SQ_ERR_NOMEM, SQ_ERR_HIP.  Synchronous (uploads with a blocking copy). */
+ * aligned, state_bytes too small, 0 < scale_slot_stride < n_heads),
+ * SQ_ERR_UNSUPPORTED (bits, d_k, d_v), SQ_ERR_NOMEM, SQ_ERR_HIP.
+ * Synchronous (uploads with a blocking copy). */
 int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out);
 
 /* Release the handle and its device table (not the borrowed buffers).
@@ -179,7 +195,8 @@ int sq_decode_step_kda(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, co
                        const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
                        const float *beta, float *o, void *stream);
 
-/* Readout without update: o = S^T q from the stored state (dequantized), for
+/* Readout without update ([P5] 空间维度: the head's output is the query read
+ * out of the state): o = S^T q from the stored state (dequantized), for
  * slots slot_ids[0..n_req).  q: DEVICE [n_req][n_heads][d_k] of q_dtype;
  * o: DEVICE fp32 [n_req][n_heads][d_v].  Does not modify the pool.  n_req == 0
  * is a no-op.  Asynchronous on `stream`.  Errors as for sq_decode_step (q and
@@ -202,6 +219,16 @@ int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, cons
  * synchronizing it. */
 int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_t *result,
                    void *stream);
+
+/* Read and clear the pool's sticky device flag.  The step, the per-channel-
+ * gate step and the store set it when an updated value (the quotient S'/s for
+ * codes, S' for unquantized heads) is not finite, which only non-finite or
+ * huge inputs cause; the stored result then follows the rule above (NaN ->
+ * code 0, +-Inf -> +-Q).  Synchronizes `stream` first (host-blocking).
+ * Returns SQ_OK if no such value was met since the pool was made or the flag
+ * last read, SQ_ERR_DEVICE if one was; SQ_ERR_INVALID (null pool, another
+ * device current), SQ_ERR_HIP. */
+int sq_pool_last_device_error(sq_pool *pool, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *sq_status_string(int status);

@@ -72,14 +72,17 @@ struct sq_pool {
     std::vector<int64_t> off;
     uint64_t slab;
     const float *rsc, *csc;
+    int64_t sstride;          // scale_slot_stride (0 = factors shared by every slot)
     uint8_t *state;
     uint64_t state_bytes;
     int device;
     void *dtab;               // device: int64 head_off[H] | int32 heads grouped by class | u8 bits[H]
                               //         | pad to 4 | int32 slot stamps[n_slots] | int32 generation
+                              //         | int32 sticky error word
     int64_t *d_off;
     uint8_t *d_bits;
     int32_t *d_stamps;        // sq_check_slots' per-slot stamps + generation, zeroed at alloc
+    int32_t *d_err;           // set by the kernels (bit 0: a non-finite updated value), zeroed at alloc
     int32_t *d_heads[kNumClasses];
     int32_t n_class[kNumClasses];
 };
@@ -116,6 +119,7 @@ static int pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     const sq_pool_desc &d = *desc;
     if (d.n_slots < 1 || d.n_heads < 1 || !d.head_bits || !d.state) return SQ_ERR_INVALID;
     if (!d.row_scale || !d.col_scale) return SQ_ERR_INVALID;
+    if (d.scale_slot_stride != 0 && d.scale_slot_stride < d.n_heads) return SQ_ERR_INVALID;
     if (!aligned(d.state, 256) || !aligned(d.row_scale, 16) || !aligned(d.col_scale, 16))
         return SQ_ERR_INVALID;
     std::vector<int64_t> off;
@@ -136,13 +140,14 @@ static int pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     p->slab = slab;
     p->rsc = d.row_scale;
     p->csc = d.col_scale;
+    p->sstride = d.scale_slot_stride;
     p->state = static_cast<uint8_t *>(d.state);
     p->state_bytes = d.state_bytes;
 
     // host image of the device table: offsets, then head ids grouped by width
     const size_t H = (size_t)d.n_heads;
     const size_t stamps_at = (H * 13 + 3) / 4 * 4;
-    std::vector<unsigned char> img(stamps_at + ((size_t)d.n_slots + 1) * 4, 0);
+    std::vector<unsigned char> img(stamps_at + ((size_t)d.n_slots + 2) * 4, 0);
     memcpy(img.data(), off.data(), H * 8);
     int32_t *heads = reinterpret_cast<int32_t *>(img.data() + H * 8);
     size_t pos = 0;
@@ -176,6 +181,7 @@ static int pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     for (int c = 0; c < kNumClasses; c++) p->d_heads[c] = dheads + start[c];
     p->d_bits = static_cast<unsigned char *>(p->dtab) + H * 12;
     p->d_stamps = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(p->dtab) + stamps_at);
+    p->d_err = p->d_stamps + d.n_slots + 1;
     *out = p;
     return SQ_OK;
 }
@@ -218,6 +224,9 @@ static sqk::StepArgs base_args(const sq_pool *p, const int32_t *slot_ids)
     a.slot_ids = slot_ids;
     a.rsc = p->rsc;
     a.csc = p->csc;
+    a.rstride = (uint64_t)p->sstride * (uint64_t)p->dk;
+    a.cstride = (uint64_t)p->sstride * (uint64_t)p->dv;
+    a.err = p->d_err;
     return a;
 }
 
@@ -367,6 +376,22 @@ int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_
     return SQ_OK;
 }
 
+int sq_pool_last_device_error(sq_pool *pool, void *stream)
+{
+    if (!pool) return SQ_ERR_INVALID;
+    if (int st = check_device(pool)) return st;
+    // wait for the caller's work on the pool, then read and clear the word
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SQ_ERR_HIP;
+    int32_t word = 0;
+    if (hipMemcpy(&word, pool->d_err, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        return SQ_ERR_HIP;
+    if (word == 0) return SQ_OK;
+    const int32_t zero = 0;
+    if (hipMemcpy(pool->d_err, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+        return SQ_ERR_HIP;
+    return SQ_ERR_DEVICE;
+}
+
 const char *sq_status_string(int status)
 {
     switch (status) {
@@ -375,6 +400,7 @@ const char *sq_status_string(int status)
     case SQ_ERR_UNSUPPORTED: return "unsupported bit width or shape";
     case SQ_ERR_HIP: return "HIP runtime error";
     case SQ_ERR_NOMEM: return "out of memory";
+    case SQ_ERR_DEVICE: return "a kernel met a non-finite value (NaN or infinity)";
     default: return "unknown status";
     }
 }

@@ -31,6 +31,7 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <type_traits>
+#include <utility>
 #include <stdint.h>
 
 #include "sq_launch.h"
@@ -145,7 +146,8 @@ template <int BITS>
 __device__ __forceinline__ float clamp_code(float z)
 {
     // symmetric range [1, 2^b - 1] in excess form; the upper bound of the
-    // 8-bit range is the conversion's own saturation.  NaN -> 1 (in range).
+    // 8-bit range is the conversion's own saturation.  Callers map a NaN to
+    // code 0 (OFF) before this.
     if constexpr (BITS == 8) return fmaxf(z, 1.0f);
     else return __builtin_amdgcn_fmed3f(z, 1.0f, (float)((1 << BITS) - 1));
 }
@@ -215,39 +217,52 @@ __device__ __forceinline__ void encode(const float (&z)[16], uint32_t (&d)[fw<BI
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) uint8_t gbyte;  // global memory
 
 // Tile blocks are streamed: read once, written once, never reused by this
 // launch, so they may bypass cache retention (nontemporal hint).
-template <int BITS, bool NT>
-__device__ __forceinline__ void load_block(const uint8_t *p, uint32_t (&d)[fw<BITS>() / 2])
+template <int BITS, bool NT, typename B>
+__device__ __forceinline__ void load_block(const B *p, uint32_t (&d)[fw<BITS>() / 2])
 {
+    using U2 = typename std::conditional<std::is_same<B, gbyte>::value,
+                                         const __attribute__((address_space(1))) u32x2, const u32x2>::type;
+    using U1 = typename std::conditional<std::is_same<B, gbyte>::value,
+                                         const __attribute__((address_space(1))) uint32_t, const uint32_t>::type;
+    using U4 = typename std::conditional<std::is_same<B, gbyte>::value,
+                                         const __attribute__((address_space(1))) u32x4, const u32x4>::type;
     if constexpr (BITS == 4) {
-        const u32x2 *q = reinterpret_cast<const u32x2 *>(p);
+        U2 *q = reinterpret_cast<U2 *>(p);
         const u32x2 x = NT ? __builtin_nontemporal_load(q) : *q;
         d[0] = x.x; d[1] = x.y;
     } else if constexpr (BITS == 6) {
-        const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+        U1 *q = reinterpret_cast<U1 *>(p);
 #pragma unroll
         for (int w = 0; w < 3; w++) d[w] = NT ? __builtin_nontemporal_load(q + w) : q[w];
     } else {
 #pragma unroll
         for (int w = 0; w < fw<BITS>() / 2; w += 4) {
-            const u32x4 *q = reinterpret_cast<const u32x4 *>(p + 4 * w);
+            U4 *q = reinterpret_cast<U4 *>(p + 4 * w);
             const u32x4 x = NT ? __builtin_nontemporal_load(q) : *q;
             d[w] = x.x; d[w + 1] = x.y; d[w + 2] = x.z; d[w + 3] = x.w;
         }
     }
 }
 
-template <int BITS, bool NT>
-__device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[fw<BITS>() / 2])
+template <int BITS, bool NT, typename B>
+__device__ __forceinline__ void store_block(B *p, const uint32_t (&d)[fw<BITS>() / 2])
 {
+    using U2 = typename std::conditional<std::is_same<B, gbyte>::value,
+                                         __attribute__((address_space(1))) u32x2, u32x2>::type;
+    using U1 = typename std::conditional<std::is_same<B, gbyte>::value,
+                                         __attribute__((address_space(1))) uint32_t, uint32_t>::type;
+    using U4 = typename std::conditional<std::is_same<B, gbyte>::value,
+                                         __attribute__((address_space(1))) u32x4, u32x4>::type;
     if constexpr (BITS == 4) {
-        u32x2 *q = reinterpret_cast<u32x2 *>(p);
+        U2 *q = reinterpret_cast<U2 *>(p);
         const u32x2 x = {d[0], d[1]};
         if (NT) __builtin_nontemporal_store(x, q); else *q = x;
     } else if constexpr (BITS == 6) {
-        uint32_t *q = reinterpret_cast<uint32_t *>(p);
+        U1 *q = reinterpret_cast<U1 *>(p);
 #pragma unroll
         for (int w = 0; w < 3; w++) {
             if (NT) __builtin_nontemporal_store(d[w], q + w); else q[w] = d[w];
@@ -255,7 +270,7 @@ __device__ __forceinline__ void store_block(uint8_t *p, const uint32_t (&d)[fw<B
     } else {
 #pragma unroll
         for (int w = 0; w < fw<BITS>() / 2; w += 4) {
-            u32x4 *q = reinterpret_cast<u32x4 *>(p + 4 * w);
+            U4 *q = reinterpret_cast<U4 *>(p + 4 * w);
             const u32x4 x = {d[w], d[w + 1], d[w + 2], d[w + 3]};
             if (NT) __builtin_nontemporal_store(x, q); else *q = x;
         }
@@ -302,20 +317,32 @@ __device__ __forceinline__ float wave_sum(float x)
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kXcdGroupMin = 64;
 
+// floor(i / d) for d >= 1 from m = ceil(2^32 / d) (host-computed, 0 for
+// d = 1): umulhi(i, m) is floor(i / d) or one more.
+__device__ __forceinline__ uint32_t div_magic(uint32_t i, uint32_t d, uint32_t m)
+{
+    if (d == 1) return i;
+    uint32_t q = __umulhi(i, m);
+    if (q * d > i) q--;
+    return q;
+}
+
 // Tile (n, h) of workgroup blockIdx.x for n_req requests x H heads; false if
-// the workgroup has no tile.
-__device__ __forceinline__ bool xcd_tile(uint32_t n_req, uint32_t H, uint32_t &n, uint32_t &h)
+// the workgroup has no tile.  xm[x] is the reciprocal of XCD x's head count
+// (H >= kXcdGroupMin) or, in xm[0], of H itself (smaller pools).
+__device__ __forceinline__ bool xcd_tile(uint32_t n_req, uint32_t H, const uint32_t (&xm)[8],
+                                         uint32_t &n, uint32_t &h)
 {
     const uint32_t x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
     if (H >= kXcdGroupMin) {
         const uint32_t h0 = (uint32_t)((uint64_t)x * H / kXcds);
         const uint32_t hx = (uint32_t)((uint64_t)(x + 1) * H / kXcds) - h0;
-        n = i / hx;
+        n = div_magic(i, hx, xm[x]);
         h = h0 + (i - n * hx);
         return n < n_req;
     }
     const uint32_t total = n_req * H, per = (total + kXcds - 1) / kXcds, b = x * per + i;
-    n = b / H;
+    n = div_magic(b, H, xm[0]);
     h = b - n * H;
     return i < per && b < total;
 }
@@ -326,26 +353,37 @@ __host__ __forceinline__ uint32_t xcd_grid(uint32_t n_req, uint32_t H)
     return (n_req * H + kXcds - 1) / kXcds * kXcds;
 }
 
+static uint32_t magic_of(uint32_t d) { return d <= 1 ? 0u : (uint32_t)(((1ull << 32) + d - 1) / d); }
+
+// the reciprocals xcd_tile needs for H heads
+static void xcd_magic(uint32_t H, uint32_t (&xm)[8])
+{
+    for (uint32_t x = 0; x < kXcds; x++) {
+        if (H >= kXcdGroupMin) {
+            const uint32_t h0 = (uint32_t)((uint64_t)x * H / kXcds);
+            xm[x] = magic_of((uint32_t)((uint64_t)(x + 1) * H / kXcds) - h0);
+        } else {
+            xm[x] = magic_of(H);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- d = 128 step
 //
-// Shared memory of one tile.  Two bodies use it: tile128 (the fused launch
-// over 4/6/8-bit and FP16 tiles, codes held as packed halves; below) and
-// tile128_wide (FP32- and BF16-state tiles, 256 threads).
+// Shared memory of one FP32- or BF16-state tile (tile128_wide, 256 threads).
 
-struct Smem128 {
-    alignas(16) float w[128];      // per-row factors k_i r_i (wide tiles: k_i)
-    alignas(16) float g[128];      // q_i r_i (wide tiles: q_i)
-    alignas(16) float a[128];      // beta k_i / r_i (wide tiles: beta k_i)
-    alignas(16) float4 wg[128];    // per-row {w 2^-s0, w 2^-s1, g 2^-s0, g 2^-s1} (half codes)
+struct SmemWide {
+    alignas(16) float w[128];      // per-row factors k_i (times alpha_i with a per-channel gate)
+    alignas(16) float g[128];      // q_i (times alpha_i)
+    alignas(16) float a[128];      // beta k_i
     alignas(16) float red[8][2][128];  // [row group][u, y][column] partial sums
     alignas(16) float b[128];      // per-column (v_j - alpha u_j) / c_j
     alignas(8) float2 vc[128];     // per-column {v_j, c_j}, staged at the start
     float sum[2][3];               // per-wave partials of q.k, sum w, sum g
 };
 
-// Per-key-channel gate: pass 2 needs a per-row gate.  pa[i] = {beta k_i / r_i,
-// alpha_i 2^-s0, alpha_i 2^-s1, OFF (1 - alpha_i)}.
-struct Smem128K : Smem128 {
+// Per-key-channel gate: pass 2 needs a per-row gate.  pa[i] = {beta k_i, alpha_i, 0, 0}.
+struct SmemWideK : SmemWide {
     alignas(16) float4 pa[128];
 };
 
@@ -481,7 +519,9 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
 #pragma unroll
     for (int c = 0; c < CPL; c++) b[c] = sm.b[j0 + c];
 
-    // pass 2: S' = gate S + a_i b_j, rounded to the storage format, stored in place
+    // pass 2: S' = gate S + a_i b_j, rounded to the storage format, stored in
+    // place; a non-finite value is recorded in the pool's sticky flag
+    bool nf = false;
 #pragma unroll
     for (int m = 0; m < NI; m++) {
         const int i0 = 4 * (rgp * NI + m);
@@ -498,7 +538,10 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
                 gi = alpha;
             }
 #pragma unroll
-            for (int c = 0; c < CPL; c++) z[r][c] = fmaf(gi, elem(m, r, c), ai * b[c]);
+            for (int c = 0; c < CPL; c++) {
+                z[r][c] = fmaf(gi, elem(m, r, c), ai * b[c]);
+                nf |= !__builtin_isfinite(z[r][c]);
+            }
         }
         uint32_t o4[4];
         if constexpr (FMT == 32) {
@@ -516,6 +559,7 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
         }
         *reinterpret_cast<u32x4 *>(span + (long)m * ROW_BYTES) = u32x4{o4[0], o4[1], o4[2], o4[3]};
     }
+    if (__ballot(nf) && lane == 0) atomicOr(a.err, 1);
 }
 
 // ---------------------------------------------------------------- packed-half codes
@@ -523,14 +567,15 @@ __device__ __forceinline__ void tile128_wide(const StepArgs &a, int n, int h, SM
 // For 4/6/8-bit codes and FP16 pivots a thread keeps its 64 elements as 32
 // dwords of packed 16-bit halves.  A code n is placed in the low mantissa
 // bits of a half whose exponent field is zero, so the half is exactly the
-// binary16 subnormal n * 2^s (s = -24, or -22 / -20 where the field sits 2 /
-// 4 bits up in its half); v_fma_mix_f32 takes it as an exact fp32 operand.
-// The power of two 2^-s is folded into the per-row weights (pass 1) and into
-// the gate (pass 2), so the codes need only masks, shifts and byte permutes.
-// FP16 pivot halves are their own values (s = 0).
+// binary16 subnormal n * 2^s (s = -24, or -20 where the field sits 4 bits
+// up in its half); v_fma_mix_f32 takes it as an exact fp32 operand.  The
+// power of two depends on the row of the element only, so it is folded into
+// the per-row weights (pass 1) and into the per-row gate (pass 2), and the
+// codes need only masks, shifts and byte permutes.  FP16 pivot halves are
+// their own values (s = 0).
 //
 // HalfPos<BITS>: element e = 4*col + row of a block sits in half sel(e) of
-// packed dword k(e), with scale class cls(e) (2^s0 or 2^s1).
+// packed dword k(e); row r of the block has the power of two 2^s(r).
 
 template <int BITS>
 struct HalfPos;
@@ -538,32 +583,33 @@ template <>
 struct HalfPos<8> {  // dword 2c + (r & 1) = rows {0,2} or {1,3} of column c
     static constexpr int k(int e) { return 2 * (e >> 2) + (e & 1); }
     static constexpr int sel(int e) { return (e >> 1) & 1; }
-    static constexpr int cls(int) { return 0; }
-    static constexpr int s0 = -24, s1 = -24;
+    static constexpr int s(int) { return -24; }
+};
+template <>
+struct HalfPos<6> {  // dword 2c + (r & 1): rows {0,2} or {1,3} of column c; rows 0, 1 4 bits up
+    static constexpr int k(int e) { return 2 * (e >> 2) + (e & 1); }
+    static constexpr int sel(int e) { return (e >> 1) & 1; }
+    static constexpr int s(int r) { return r < 2 ? -20 : -24; }
 };
 template <>
 struct HalfPos<4> {  // dword 4(c/2) + r = row r of columns c, c+1; odd rows 4 bits up
     static constexpr int k(int e) { return 4 * (e >> 3) + (e & 3); }
     static constexpr int sel(int e) { return (e >> 2) & 1; }
-    static constexpr int cls(int e) { return e & 1; }
-    static constexpr int s0 = -24, s1 = -20;
-};
-template <>
-struct HalfPos<6> {  // field pairs (0,3) (1,4) (2,5) (6,9) (7,10) (8,11) (12,15) (13,14)
-    static constexpr int kk[16] = {0, 1, 2, 0, 1, 2, 3, 4, 5, 3, 4, 5, 6, 7, 7, 6};
-    static constexpr int ss[16] = {0, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 0, 0, 1, 1};
-    static constexpr int k(int e) { return kk[e]; }
-    static constexpr int sel(int e) { return ss[e]; }
-    static constexpr int cls(int e) { return (ss[e] && e != 14) ? 1 : 0; }
-    static constexpr int s0 = -24, s1 = -22;
+    static constexpr int s(int r) { return (r & 1) ? -20 : -24; }
 };
 template <>
 struct HalfPos<16> {
     static constexpr int k(int e) { return e >> 1; }
     static constexpr int sel(int e) { return e & 1; }
-    static constexpr int cls(int) { return 0; }
-    static constexpr int s0 = 0, s1 = 0;
+    static constexpr int s(int) { return 0; }
 };
+
+// 2^-s(r): the factor that turns a half of row r back into its code
+template <int BITS>
+constexpr float unscale(int r)
+{
+    return HalfPos<BITS>::s(r) == 0 ? 1.0f : (HalfPos<BITS>::s(r) == -24 ? 16777216.0f : 1048576.0f);
+}
 
 template <int BITS>
 __device__ __forceinline__ void to_halves(const uint32_t (&d)[fw<BITS>() / 2], uint32_t (&hv)[8])
@@ -584,15 +630,17 @@ __device__ __forceinline__ void to_halves(const uint32_t (&d)[fw<BITS>() / 2], u
             hv[4 * w + 3] = p & 0x00f000f0u;
         }
     } else if constexpr (BITS == 6) {
-        constexpr uint32_t M = 0x00fc003fu;  // a field at bits 0-5 and one at 18-23
-        hv[0] = d[0] & M;
-        hv[1] = (d[0] >> 6) & M;
-        hv[2] = __builtin_amdgcn_alignbit(d[1], d[0], 12) & M;
-        hv[3] = (d[1] >> 4) & M;
-        hv[4] = __builtin_amdgcn_alignbit(d[2], d[1], 10) & M;
-        hv[5] = __builtin_amdgcn_alignbit(d[2], d[1], 16) & M;
-        hv[6] = (d[2] >> 8) & M;
-        hv[7] = __builtin_amdgcn_ubfe(d[2], 14, 6) | ((d[2] >> 4) & 0x003f0000u);
+        // column c is the 24-bit group at bit 24c of the 96-bit block: rows
+        // 0/2 and 1/3 are pairs 12 bits apart, moved to bits 4 and 16
+        constexpr uint32_t M = 0x003f03f0u;
+        hv[0] = (d[0] << 4) & M;
+        hv[1] = (d[0] >> 2) & M;
+        hv[2] = __builtin_amdgcn_alignbit(d[1], d[0], 20) & M;
+        hv[3] = __builtin_amdgcn_alignbit(d[1], d[0], 26) & M;
+        hv[4] = __builtin_amdgcn_alignbit(d[2], d[1], 12) & M;
+        hv[5] = __builtin_amdgcn_alignbit(d[2], d[1], 18) & M;
+        hv[6] = (d[2] >> 4) & M;
+        hv[7] = (d[2] >> 10) & M;
     } else {
 #pragma unroll
         for (int w = 0; w < 8; w++) hv[w] = d[w];
@@ -607,68 +655,290 @@ __device__ __forceinline__ float half_of(uint32_t x, int sel)
     return sel ? __high2float(hh) : __low2float(hh);
 }
 
+// ---------------------------------------------------------------- requantization
+//
+// The updated value arrives as z = S'/s in excess form, less a bias: 1 for
+// 4/6-bit codes (so that the conversion's saturation at 0 is the lower bound
+// of the symmetric range) and 0 for 8-bit codes (so that its saturation at
+// 255 is the upper bound).  v_cvt_pk_u8_f32 rounds half to even and
+// saturates to [0, 255]; the bound it cannot enforce is checked on the block's
+// largest (4/6-bit) or smallest (8-bit) value, and only a block that crosses
+// it, or holds a NaN, is converted again: clamped explicitly, with a NaN
+// quotient taken as code 0 (an infinite one saturates like any other).
+
+template <int BITS>
+constexpr float kBias = BITS == 8 ? 0.0f : 1.0f;
+
+// NaN-propagating three-way extremes (v_maximum3_f32 / v_minimum3_f32): a NaN
+// anywhere makes the result NaN, so that the range check below catches it.
+__device__ __forceinline__ float fmax3(float a, float b, float c)
+{
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float fmin3(float a, float b, float c)
+{
+    return __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c);
+}
+
+// Encode one block whose values z(e) are produced on demand by zf, one output
+// group at a time (a column of 8- or 6-bit codes, two columns of 4-bit
+// codes), so that at most eight of them are alive at once.  CLAMP applies the
+// range explicitly first.  Returns the block's largest (4/6-bit) or smallest
+// (8-bit) value for the range check.
+template <int BITS, bool CLAMP, typename ZF>
+__device__ __forceinline__ float encode_block(ZF zf, uint32_t (&d)[fw<BITS>() / 2])
+{
+    auto cl = [](float x) {
+        if constexpr (!CLAMP) return x;
+        else if constexpr (BITS == 8) return fmaxf(x, 1.0f);
+        else return __builtin_amdgcn_fmed3f(x, 0.0f, (float)((1 << BITS) - 2));
+    };
+    float ext = 0.0f;
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const float z0 = zf(4 * c), z1 = zf(4 * c + 1), z2 = zf(4 * c + 2), z3 = zf(4 * c + 3);
+            uint32_t x = pk_u8(cl(z0), 0, 0u);
+            x = pk_u8(cl(z1), 1, x);
+            x = pk_u8(cl(z2), 2, x);
+            d[c] = pk_u8(cl(z3), 3, x);
+            ext = c == 0 ? fmin3(fmin3(z0, z1, z2), z3, z3) : fmin3(fmin3(ext, z0, z1), z2, z3);
+        }
+    } else if constexpr (BITS == 4) {
+        // even fields into one dword of bytes, odd fields into another, then
+        // interleave the nibbles and add back the bias of every field
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            uint32_t ev = 0u, od = 0u;
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                const float ze = zf(8 * w + 2 * p), zo = zf(8 * w + 2 * p + 1);
+                ev = pk_u8(cl(ze), p, ev);
+                od = pk_u8(cl(zo), p, od);
+                ext = (w == 0 && p == 0) ? fmax3(ze, zo, zo) : fmax3(ext, ze, zo);
+            }
+            d[w] = (ev | (od << 4)) + 0x11111111u;
+        }
+    } else {
+        // four codes of a column -> four bytes (each < 63) -> one 24-bit group
+        // f0 | f1 << 6 | f2 << 12 | f3 << 18, as two byte dot products whose
+        // accumulator adds back the bias (65 = 1 + 64); the four 3-byte groups
+        // are then spliced into three dwords with byte permutes
+        uint32_t g[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const float z0 = zf(4 * c), z1 = zf(4 * c + 1), z2 = zf(4 * c + 2), z3 = zf(4 * c + 3);
+            uint32_t x = pk_u8(cl(z0), 0, 0u);
+            x = pk_u8(cl(z1), 1, x);
+            x = pk_u8(cl(z2), 2, x);
+            x = pk_u8(cl(z3), 3, x);
+            const uint32_t lo12 = __builtin_amdgcn_udot4(x, 0x00004001u, 65u, false);
+            const uint32_t hi12 = __builtin_amdgcn_udot4(x, 0x40010000u, 65u, false);
+            g[c] = lo12 | (hi12 << 12);
+            ext = c == 0 ? fmax3(fmax3(z0, z1, z2), z3, z3) : fmax3(fmax3(ext, z0, z1), z2, z3);
+        }
+        d[0] = __builtin_amdgcn_perm(g[1], g[0], 0x04020100u);  // g0 bytes 0-2, g1 byte 0
+        d[1] = __builtin_amdgcn_perm(g[2], g[1], 0x05040201u);  // g1 bytes 1-2, g2 bytes 0-1
+        d[2] = __builtin_amdgcn_perm(g[3], g[2], 0x06050402u);  // g2 byte 2, g3 bytes 0-2
+    }
+    return ext;
+}
+
+// true if the block's extreme (encode_block) calls for the explicit clamp: a
+// value beyond the bound the conversion cannot enforce, or a NaN
+template <int BITS>
+__device__ __forceinline__ bool out_of_range(float ext)
+{
+    if constexpr (BITS == 8) return !(ext > 0.5f);  // rne(0.5) = 0: the code below -Q
+    // biased codes 0 .. 2^b - 2 are valid; rne(2^b - 1.5) = 2^b - 2
+    else return !(ext <= (float)((1 << BITS) - 2) + 0.5f);
+}
+
+// ---------------------------------------------------------------- d = 128 fused step
+
+// scalar load (one per wavefront) from a wave-uniform address
+template <typename U>
+__device__ __forceinline__ U sload(const U *p)
+{
+    return *(const __attribute__((address_space(4))) U *)p;
+}
+
+// Address of block m of a thread: the tile's (wave-uniform) base advanced by
+// whole 4 KB pages, plus the lane's 32-bit offset, plus an immediate below
+// 4 KB, so every load and store takes the scalar-base + 32-bit-offset form.
+// The page base is pinned to scalar registers, and the loads and the stores
+// each take their own opaque copy of the lane offset, so that the optimizer
+// does not fold the page steps into 64-bit per-block vector addresses (which
+// it would then keep alive, or spill, between the loads and the stores).
+template <uint32_t MSTEP>
+__device__ __forceinline__ gbyte *block_ptr(uint8_t *tile, uint32_t lane_off, int m)
+{
+    constexpr uint32_t PAGE = 4096;
+    const uint32_t o = (uint32_t)m * MSTEP;
+    gbyte *page = (gbyte *)(tile + o / PAGE * PAGE);
+    asm volatile("" : "+s"(page));  // scalar registers, recomputed at each use
+    return page + lane_off + o % PAGE;
+}
+
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Store a thread's block at page + off + IMM (scalar base, 32-bit lane
+// offset, immediate below 4 KB).  Written out because the compiler gives
+// these stores 64-bit vector addresses, one more instruction each.  A store
+// has no register results, so no wait depends on it.
+template <int BITS, bool NT, int IMM>
+__device__ __forceinline__ void store_block_asm(const uint8_t *page, uint32_t off,
+                                                const uint32_t (&d)[fw<BITS>() / 2])
+{
+    static_assert(IMM >= 0 && IMM + 16 < 4096, "immediate offset");
+    if constexpr (BITS == 4) {
+        const u32x2 x = {d[0], d[1]};
+        if constexpr (NT)
+            asm volatile("global_store_dwordx2 %0, %1, %2 offset:%3 nt" ::"v"(off), "v"(x), "s"(page), "i"(IMM));
+        else
+            asm volatile("global_store_dwordx2 %0, %1, %2 offset:%3" ::"v"(off), "v"(x), "s"(page), "i"(IMM));
+    } else if constexpr (BITS == 6) {
+        const u32x3 x = {d[0], d[1], d[2]};
+        if constexpr (NT)
+            asm volatile("global_store_dwordx3 %0, %1, %2 offset:%3 nt" ::"v"(off), "v"(x), "s"(page), "i"(IMM));
+        else
+            asm volatile("global_store_dwordx3 %0, %1, %2 offset:%3" ::"v"(off), "v"(x), "s"(page), "i"(IMM));
+    } else {
+#pragma unroll
+        for (int w = 0; w < fw<BITS>() / 2; w += 4) {
+            const u32x4 x = {d[w], d[w + 1], d[w + 2], d[w + 3]};
+            if constexpr (NT) {
+                if (w == 0)
+                    asm volatile("global_store_dwordx4 %0, %1, %2 offset:%3 nt" ::"v"(off), "v"(x), "s"(page), "i"(IMM));
+                else
+                    asm volatile("global_store_dwordx4 %0, %1, %2 offset:%3 nt" ::"v"(off), "v"(x), "s"(page), "i"(IMM + 16));
+            } else {
+                if (w == 0)
+                    asm volatile("global_store_dwordx4 %0, %1, %2 offset:%3" ::"v"(off), "v"(x), "s"(page), "i"(IMM));
+                else
+                    asm volatile("global_store_dwordx4 %0, %1, %2 offset:%3" ::"v"(off), "v"(x), "s"(page), "i"(IMM + 16));
+            }
+        }
+    }
+}
+
+// f(std::integral_constant<int, m>) for m = 0 .. N - 1, in order
+template <typename F, int... Ms>
+__device__ __forceinline__ void for_blocks(F &&f, std::integer_sequence<int, Ms...>)
+{
+    (f(std::integral_constant<int, Ms>{}), ...);
+}
+
+__device__ __forceinline__ uint32_t opaque(uint32_t x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// The last two steps of a 64-lane sum after the in-row DPP steps: row 0 is
+// added into row 1 and row 2 into row 3, then rows 0-1 into rows 2 and 3, so
+// row 3 (lanes 48-63) holds the total.  One instruction each (a lane outside
+// the row mask keeps its value).
+__device__ __forceinline__ float rows_to_row3(float x)
+{
+    asm volatile("s_nop 1\n\t"
+                 "v_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
+                 : "+v"(x));
+    return x;
+}
+
+// sum over the 64 lanes of a wave, held by lanes 48-63
+__device__ __forceinline__ float wave_sum_row3(float x)
+{
+    x += dpp<0xb1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4e>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);  // row_half_mirror: sums of 8
+    x += dpp<0x140>(x);  // row_mirror: every lane holds its row's sum
+    return rows_to_row3(x);
+}
+
+// Shared memory of one fused tile.
+struct SmemFused {
+    alignas(16) float2 wg[128];        // per-row {w_i 2^-s, g_i 2^-s}, w = k_i r_i, g = q_i r_i
+    alignas(16) float a[128];          // per-row beta k_i / r_i
+    alignas(16) float red[8][2][128];  // [row group][u, y][column] partial sums
+    alignas(16) float b[128];          // per-column (v_j - alpha u_j) / c_j
+    alignas(8) float2 vc[128];         // per-column {v_j, c_j}
+    alignas(16) float sum[2][4];       // per-wave totals of q.k, sum w, sum g (from lanes 48-63)
+};
+
+// Per-key-channel gate: pass 2 takes a per-row gate.  pa[i] = {beta k_i / r_i,
+// alpha_i 2^-s, OFF (1 - alpha_i) - bias, 0}.
+struct SmemFusedK : SmemFused {
+    alignas(16) float4 pa[128];
+};
+
 template <int BITS, typename T, bool UPDATE, bool CHG, int TPB, typename SM>
-__device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
+__device__ __forceinline__ void tile128(const StepArgs &a, uint32_t n, uint32_t h, SM &sm)
 {
     // TPB threads per tile: RG = TPB / 32 row groups, MB = 32 / RG blocks per thread
     constexpr int RG = TPB / 32, MB = 32 / RG;
+    static_assert(TPB == 128 || TPB == 256, "128 or 256 threads per tile");
     using P = HalfPos<BITS>;
     constexpr int W = fw<BITS>() / 2;
     constexpr bool QUANT = BITS <= 8;
     constexpr float OFF = QUANT ? (float)(1 << (BITS - 1)) : 0.0f;
-    constexpr int BLK_BYTES = 2 * fw<BITS>();
-    constexpr bool NT = QUANT;  // code tiles stream nontemporally (measured faster)
-    constexpr float SC0 = P::s0 == 0 ? 1.0f : (P::s0 == -24 ? 16777216.0f : 0.0f);
-    constexpr float SC1 = P::s1 == 0 ? 1.0f : (P::s1 == -24 ? 16777216.0f : (P::s1 == -22 ? 4194304.0f : 1048576.0f));
-    static_assert(SC0 > 0.0f, "scale");
+    constexpr float BIAS = QUANT ? kBias<BITS> : 0.0f;
+    constexpr uint32_t BLK = 2 * fw<BITS>();   // bytes of one 4x4 block
+    constexpr uint32_t MSTEP = RG * 32 * BLK;  // bytes between a thread's blocks
+    constexpr bool NT = QUANT;                 // code tiles stream nontemporally (measured faster)
 
     const int t = threadIdx.x;
-    const int cb = t & 31, rg = t >> 5;
-    const long nh = (long)n * a.H + h;
-    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
-    const T *q = reinterpret_cast<const T *>(a.q);
-    const T *k = reinterpret_cast<const T *>(a.k);
-    const T *v = reinterpret_cast<const T *>(a.v);
+    const int cb = t & 31, rg = t >> 5, tr = t & 127;
+    const size_t nh = (size_t)n * (uint32_t)a.H + h;
+    const int32_t slot = sload(a.slot_ids + n);
+    uint8_t *tile = a.pool + (uint64_t)slot * a.slab + (uint64_t)sload(a.head_off + h);
+    const T *q = reinterpret_cast<const T *>(a.q) + nh * 128;
+    const T *k = reinterpret_cast<const T *>(a.k) + nh * 128;
+    const T *v = reinterpret_cast<const T *>(a.v) + nh * 128;
+    const float *rsc = a.rsc + (size_t)slot * a.rstride + (size_t)h * 128;
+    const float *csc = a.csc + (size_t)slot * a.cstride + (size_t)h * 128;
 
     // the per-row (q, k, r, gate) and per-column (v, c) inputs of thread t
     // are loaded before the tile: vector loads complete in issue order, so
     // the row factors can be formed while the tile is still in flight
-    const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
-    const float beta = UPDATE ? a.beta[nh] : 0.0f;
-    // row and column tr = t % 128 (with 256 threads, waves 2 and 3 repeat
-    // waves 0 and 1 here and write the same values)
-    static_assert(TPB == 128 || TPB == 256, "128 or 256 threads per tile");
-    const int tr = t & 127;
-    const float qi = ld1(q, nh * 128 + tr);
-    const float ki = UPDATE ? ld1(k, nh * 128 + tr) : 0.0f;
-    const float rs = QUANT ? a.rsc[(long)h * 128 + tr] : 1.0f;
+    const float alpha = UPDATE && !CHG ? sload(a.alpha + nh) : 1.0f;
+    const float beta = UPDATE ? sload(a.beta + nh) : 0.0f;
+    // row and column tr (with 256 threads, waves 2 and 3 repeat waves 0 and 1
+    // here and write the same values)
+    const float qi = ld1(q, tr);
+    const float ki = UPDATE ? ld1(k, tr) : 0.0f;
+    const float rs = QUANT ? rsc[tr] : 1.0f;
     const float gate = CHG ? a.alpha[nh * 128 + tr] : 1.0f;
-    const float vj = UPDATE ? ld1(v, nh * 128 + tr) : 0.0f;
-    const float cjs = QUANT ? a.csc[(long)h * 128 + tr] : 1.0f;
+    const float vj = UPDATE ? ld1(v, tr) : 0.0f;
+    const float cjs = QUANT ? csc[tr] : 1.0f;
 
     // block (rg + RG m, cb) of the tile; the 64 lanes of a wave cover 64
-    // consecutive blocks for every m (global loads measured faster on gfx950
-    // than buffer loads with a per-tile resource)
+    // consecutive blocks for every m
+    const uint32_t lane_off = opaque((uint32_t)(rg * 32 + cb) * BLK);
     uint32_t d[MB][W];
 #pragma unroll
-    for (int m = 0; m < MB; m++)
-        load_block<BITS, NT>(tile + (long)((rg + RG * m) * 32 + cb) * BLK_BYTES, d[m]);
+    for (int m = 0; m < MB; m++) load_block<BITS, NT>(block_ptr<MSTEP>(tile, lane_off, m), d[m]);
 
-    // per-channel gate: alpha_i scales row i of the weights, the column terms
-    // take alpha = 1 (u = (diag(alpha) S)^T k, o = y + beta (q.k) (v - u))
+    // per-row factors; the row's power of two 2^-s is folded in (see HalfPos)
     {
+        const float us = (tr & 3) == 0 ? unscale<BITS>(0)
+                       : (tr & 3) == 1 ? unscale<BITS>(1)
+                       : (tr & 3) == 2 ? unscale<BITS>(2) : unscale<BITS>(3);
         const float wi = ki * rs * gate, gi = qi * rs * gate;
-        sm.wg[tr] = make_float4(wi * SC0, wi * SC1, gi * SC0, gi * SC1);
+        sm.wg[tr] = make_float2(wi * us, gi * us);
         const float ai = QUANT ? beta * ki * __builtin_amdgcn_rcpf(rs) : beta * ki;
-        if constexpr (CHG) sm.pa[tr] = make_float4(ai, gate * SC0, gate * SC1, OFF * (1.0f - gate));
+        if constexpr (CHG) sm.pa[tr] = make_float4(ai, gate * us, OFF * (1.0f - gate) - BIAS, 0.0f);
         else if (UPDATE) sm.a[tr] = ai;
         sm.vc[tr] = make_float2(vj, cjs);
-        const float s0 = wave_sum(qi * ki), s1 = wave_sum(wi), s2 = wave_sum(gi);
-        if (t < 128 && (t & 63) == 0) {
-            sm.sum[t >> 6][0] = s0;
-            sm.sum[t >> 6][1] = s1;
-            sm.sum[t >> 6][2] = s2;
-        }
+        // a non-finite row factor or gate sets the pool's sticky flag
+        if (__ballot(!__builtin_isfinite(fabsf(ai) + fabsf(CHG ? gate : alpha))) && (t & 63) == 0)
+            a.err[0] = 1;
+        const float s0 = wave_sum_row3(qi * ki), s1 = wave_sum_row3(wi), s2 = wave_sum_row3(gi);
+        if (t < 128 && (t & 63) == 48)
+            *reinterpret_cast<float4 *>(&sm.sum[t >> 6][0]) = make_float4(s0, s1, s2, 0.0f);
     }
     __syncthreads();
 
@@ -679,55 +949,54 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
     // The two reductions (pass 1, then the column finalisation) run at a
     // raised wave priority: a tile whose data has arrived gets through its two
     // barriers sooner, while other waves on the SIMD are still waiting for
-    // memory.  Measured on 70 x 2304 pools: -1.9 % per step on the serving
-    // mix, -3.7 % all-6-bit, -4.5 % on the 4-bit-heavy mix; raising it from
-    // the start of the tile instead gained nothing.
+    // memory.
     __builtin_amdgcn_s_setprio(2);
 
     // pass 1: partial sums of w_i n_ij and g_i n_ij over this thread's rows
     float pu[4] = {0, 0, 0, 0}, py[4] = {0, 0, 0, 0};
+    const float2 *wgp = &sm.wg[4 * rg];
 #pragma unroll
     for (int m = 0; m < MB; m++) {
-        const int i0 = 4 * (rg + RG * m);
+        const float4 f01 = *reinterpret_cast<const float4 *>(wgp + 4 * RG * m);
+        const float4 f23 = *reinterpret_cast<const float4 *>(wgp + 4 * RG * m + 2);
+        const float wr[4] = {f01.x, f01.z, f23.x, f23.z}, gr[4] = {f01.y, f01.w, f23.y, f23.w};
 #pragma unroll
-        for (int ri = 0; ri < 4; ri++) {
-            const float4 f = sm.wg[i0 + ri];
+        for (int ri = 0; ri < 4; ri++)
 #pragma unroll
             for (int cj = 0; cj < 4; cj++) {
                 const int e = 4 * cj + ri;
                 const float x = half_of(hv[m][P::k(e)], P::sel(e));
-                const float w = P::cls(e) ? f.y : f.x;
-                const float g = P::cls(e) ? f.w : f.z;
-                if (UPDATE) pu[cj] = fmaf(w, x, pu[cj]);
-                py[cj] = fmaf(g, x, py[cj]);
+                if (UPDATE) pu[cj] = fmaf(wr[ri], x, pu[cj]);
+                py[cj] = fmaf(gr[ri], x, py[cj]);
             }
-        }
     }
-    *reinterpret_cast<float4 *>(&sm.red[rg][0][4 * cb]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
+    if (UPDATE) *reinterpret_cast<float4 *>(&sm.red[rg][0][4 * cb]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
     *reinterpret_cast<float4 *>(&sm.red[rg][1][4 * cb]) = make_float4(py[0], py[1], py[2], py[3]);
     __syncthreads();
 
     // column finalisation: thread j < 128 owns column j
     if (t < 128) {
-        float U = 0.0f, Y = 0.0f;
+        float U = UPDATE ? sm.red[0][0][t] : 0.0f, Y = sm.red[0][1][t];
 #pragma unroll
-        for (int r = 0; r < RG; r++) {
-            U += sm.red[r][0][t];
+        for (int r = 1; r < RG; r++) {
+            if (UPDATE) U += sm.red[r][0][t];
             Y += sm.red[r][1][t];
         }
-        const float qk = sm.sum[0][0] + sm.sum[1][0];
-        const float Wsum = sm.sum[0][1] + sm.sum[1][1];
-        const float Gsum = sm.sum[0][2] + sm.sum[1][2];
+        const float4 s0 = *reinterpret_cast<const float4 *>(&sm.sum[0][0]);
+        const float4 s1 = *reinterpret_cast<const float4 *>(&sm.sum[1][0]);
         const float2 vc = sm.vc[t];
         const float cj = vc.y;
-        const float uj = cj * (U - OFF * Wsum);
-        const float yj = cj * (Y - OFF * Gsum);
+        const float yj = cj * (Y - OFF * (s0.z + s1.z));
         if (!UPDATE) {
             a.o[nh * 128 + t] = yj;
         } else {
+            const float uj = cj * (U - OFF * (s0.y + s1.y));
             const float e = vc.x - alpha * uj;
-            if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * qk * e);
-            sm.b[t] = QUANT ? e * __builtin_amdgcn_rcpf(cj) : e;
+            if (a.o) a.o[nh * 128 + t] = fmaf(alpha, yj, beta * (s0.x + s1.x) * e);
+            const float bj = QUANT ? e * __builtin_amdgcn_rcpf(cj) : e;
+            sm.b[t] = bj;
+            // a non-finite column factor sets the pool's sticky flag
+            if (__ballot(!__builtin_isfinite(bj)) && (t & 63) == 0) a.err[0] = 1;
         }
     }
     if (!UPDATE) return;
@@ -735,6 +1004,32 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
     __builtin_amdgcn_s_setprio(0);
     const float4 b4 = *reinterpret_cast<const float4 *>(&sm.b[4 * cb]);
     const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+
+    // pass 2: z = alpha n + a_i b_j + OFF (1 - alpha) - bias
+    const float C = OFF * (1.0f - alpha) - BIAS;
+    const float al[4] = {alpha * unscale<BITS>(0), alpha * unscale<BITS>(1), alpha * unscale<BITS>(2),
+                         alpha * unscale<BITS>(3)};
+    const float *ap = &sm.a[4 * rg];
+    const float4 *pp = nullptr;
+    if constexpr (CHG) pp = &sm.pa[4 * rg];
+
+    // z(e) of block m from a thread's halves hh, produced on demand
+    auto block_zf = [&](int m, const uint32_t (&hh)[8]) {
+        float4 fa;
+        if constexpr (!CHG) fa = *reinterpret_cast<const float4 *>(ap + 4 * RG * m);
+        return [&, m, fa](int e) -> float {
+            const int ri = e & 3, cj = e >> 2;
+            const float x = half_of(hh[P::k(e)], P::sel(e));
+            if constexpr (CHG) {
+                const float4 p = pp[4 * RG * m + ri];
+                return fmaf(p.y, x, fmaf(p.x, b[cj], p.z));
+            } else {
+                const float ar = ri == 0 ? fa.x : ri == 1 ? fa.y : ri == 2 ? fa.z : fa.w;
+                return fmaf(al[ri], x, fmaf(ar, b[cj], C));
+            }
+        };
+    };
+
     // the halves are read again in pass 2: keeping them opaque makes the
     // compiler fold the conversion into v_fma_mix_f32 there too instead of
     // keeping 64 converted floats alive across the reduction
@@ -742,38 +1037,41 @@ __device__ __forceinline__ void tile128(const StepArgs &a, int n, int h, SM &sm)
     for (int m = 0; m < MB; m++)
 #pragma unroll
         for (int w = 0; w < 8; w++) asm volatile("" : "+v"(hv[m][w]));
+    const uint32_t st_off = opaque(lane_off);  // the stores' own copy
 
-    // pass 2: z = alpha n + a_i b_j + OFF (1 - alpha), requantize, repack, store
-    const float C = OFF * (1.0f - alpha);
-    const float al0 = alpha * SC0, al1 = alpha * SC1;  // alpha n = (alpha 2^-s) (n 2^s)
-#pragma unroll
-    for (int m = 0; m < MB; m++) {
-        const int i0 = 4 * (rg + RG * m);
-        float z[16];
-#pragma unroll
-        for (int ri = 0; ri < 4; ri++) {
-            if constexpr (CHG) {
-                const float4 p = sm.pa[i0 + ri];
-#pragma unroll
-                for (int cj = 0; cj < 4; cj++) {
-                    const int e = 4 * cj + ri;
-                    const float x = half_of(hv[m][P::k(e)], P::sel(e));
-                    z[e] = fmaf(P::cls(e) ? p.z : p.y, x, fmaf(p.x, b[cj], p.w));
+    bool nf = false;
+    for_blocks(
+        [&](auto M) {
+            constexpr int m = decltype(M)::value;
+            const auto zf = block_zf(m, hv[m]);
+            uint32_t dn[W];
+            if constexpr (QUANT) {
+                if (out_of_range<BITS>(encode_block<BITS, false>(zf, dn))) {
+                    // rare (lanes whose block crosses the bound or holds a NaN):
+                    // clamp explicitly; a NaN quotient becomes code 0
+                    encode_block<BITS, true>(
+                        [&](int e) {
+                            const float x = zf(e);
+                            return x != x ? OFF - BIAS : x;
+                        },
+                        dn);
                 }
             } else {
-                const float ai = sm.a[i0 + ri];
+                // FP16 pivot: binary16, half to even; a non-finite value is recorded
 #pragma unroll
-                for (int cj = 0; cj < 4; cj++) {
-                    const int e = 4 * cj + ri;
-                    const float x = half_of(hv[m][P::k(e)], P::sel(e));
-                    z[e] = fmaf(P::cls(e) ? al1 : al0, x, fmaf(ai, b[cj], C));
+                for (int w = 0; w < 8; w++) {
+                    const float z0 = zf(2 * w), z1 = zf(2 * w + 1);
+                    nf |= !__builtin_isfinite(z0) || !__builtin_isfinite(z1);
+                    const uint32_t lo = __half_as_ushort(__float2half_rn(z0));
+                    const uint32_t hi = __half_as_ushort(__float2half_rn(z1));
+                    dn[w] = lo | (hi << 16);
                 }
             }
-        }
-        uint32_t dn[W];
-        encode<BITS>(z, dn);
-        store_block<BITS, NT>(tile + (long)((rg + RG * m) * 32 + cb) * BLK_BYTES, dn);
-    }
+            constexpr uint32_t o = (uint32_t)m * MSTEP;
+            store_block_asm<BITS, NT, (int)(o % 4096)>(tile + o / 4096 * 4096, st_off, dn);
+        },
+        std::make_integer_sequence<int, MB>{});
+    if (__ballot(nf) && (t & 63) == 0) a.err[0] = 1;
 }
 
 template <typename T, bool UPDATE, bool CHG, int TPB, int WPE>
@@ -783,11 +1081,11 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) v
     // in memory order, so tiles of every width are interleaved on each CU
     // (VALU-heavy narrow codes overlap with memory-heavy wide tiles).  FP32-
     // and BF16-state heads are skipped here and run in k_step128_wide.
-    using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
+    using SM = typename std::conditional<CHG, SmemFusedK, SmemFused>::type;
     __shared__ SM sm;
     uint32_t n, h;
-    if (!xcd_tile((uint32_t)f.a.n_req, (uint32_t)f.a.H, n, h)) return;
-    switch (f.head_bits[h]) {
+    if (!xcd_tile((uint32_t)f.a.n_req, (uint32_t)f.a.H, f.a.xm, n, h)) return;
+    switch (sload(f.head_bits + h)) {
     case 16: tile128<16, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
     case 8: tile128<8, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
     case 6: tile128<6, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
@@ -800,10 +1098,10 @@ template <int FMT, typename T, bool UPDATE, bool CHG>
 __global__ __launch_bounds__(kWideTPB) void k_step128_wide(StepArgs a)
 {
     // FP32- or BF16-state heads of a d = 128 pool (a.heads / a.Hc)
-    using SM = typename std::conditional<CHG, Smem128K, Smem128>::type;
+    using SM = typename std::conditional<CHG, SmemWideK, SmemWide>::type;
     __shared__ SM sm;
     uint32_t n, hc;
-    if (!xcd_tile((uint32_t)a.n_req, (uint32_t)a.Hc, n, hc)) return;
+    if (!xcd_tile((uint32_t)a.n_req, (uint32_t)a.Hc, a.xm, n, hc)) return;
     tile128_wide<FMT, T, UPDATE, CHG>(a, (int)n, a.heads[hc], sm);
 }
 
@@ -850,16 +1148,19 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
     const int hc = blockIdx.x - n * a.Hc;
     const int h = a.heads[hc];
     const long nh = (long)n * a.H + h;
-    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const int32_t slot = a.slot_ids[n];
+    uint8_t *tile = a.pool + (uint64_t)slot * a.slab + (uint64_t)a.head_off[h];
     const T *q = reinterpret_cast<const T *>(a.q);
     const T *k = reinterpret_cast<const T *>(a.k);
     const T *v = reinterpret_cast<const T *>(a.v);
+    const float *rsc = a.rsc + (uint64_t)slot * a.rstride + (uint64_t)h * dk;
+    const float *csc = a.csc + (uint64_t)slot * a.cstride + (uint64_t)h * dv;
     // per-channel gate: row i is scaled by alpha_i and the column terms take alpha = 1
     const float alpha = UPDATE && !CHG ? a.alpha[nh] : 1.0f;
     const float beta = UPDATE ? a.beta[nh] : 0.0f;
 
     for (int i = t; i < dk; i += 256) {
-        const float ri = QUANT ? a.rsc[(long)h * dk + i] : 1.0f;
+        const float ri = QUANT ? rsc[i] : 1.0f;
         const float ki = UPDATE ? ld1(k, nh * dk + i) : 0.0f;
         const float gate = CHG ? a.alpha[nh * dk + i] : alpha;
         sW[i] = ki * ri * (CHG ? gate : 1.0f);
@@ -881,7 +1182,7 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
             U = fmaf(sW[i], x, U);
             Y = fmaf(sG[i], x, Y);
         }
-        const float cj = QUANT ? a.csc[(long)h * dv + j] : 1.0f;
+        const float cj = QUANT ? csc[j] : 1.0f;
         const float uj = cj * U, yj = cj * Y;
         if (!UPDATE) {
             a.o[nh * dv + j] = yj;
@@ -894,6 +1195,7 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
     if (!UPDATE) return;
     __syncthreads();
     const int nblk = (dk >> 2) * (dv >> 2);
+    bool nf = false;
     for (int B = t; B < nblk; B += 256) {
         const int i0 = 4 * (B / (dv >> 2)), j0 = 4 * (B % (dv >> 2));
         uint32_t dd[W];
@@ -907,13 +1209,17 @@ __global__ __launch_bounds__(256) void k_tile_any(StepArgs a)
 #pragma unroll
             for (int ri = 0; ri < 4; ri++) {
                 const float g = sL[i0 + ri];
-                z[4 * cj + ri] = fmaf(g, f[4 * cj + ri], fmaf(sA[i0 + ri], sB[j0 + cj], OFF * (1.0f - g)));
+                float x = fmaf(g, f[4 * cj + ri], fmaf(sA[i0 + ri], sB[j0 + cj], OFF * (1.0f - g)));
+                nf |= !__builtin_isfinite(x);
+                if (QUANT && x != x) x = OFF;  // a NaN becomes code 0
+                z[4 * cj + ri] = x;
             }
         encode<BITS>(z, dd);
         uint32_t *dst = reinterpret_cast<uint32_t *>(tile + (long)B * 2 * fw<BITS>());
 #pragma unroll
         for (int w = 0; w < W; w++) dst[w] = dd[w];
     }
+    if (__ballot(nf) && (t & 63) == 0) atomicOr(a.err, 1);
 }
 
 // ---------------------------------------------------------------- store
@@ -937,24 +1243,33 @@ __global__ __launch_bounds__(256) void k_store(StepArgs a, long total_blocks)
     const int n = (int)(tix / a.Hc);
     const int h = a.heads[tix - (long)n * a.Hc];
     const long nh = (long)n * a.H + h;
-    uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const int32_t slot = a.slot_ids[n];
+    uint8_t *tile = a.pool + (uint64_t)slot * a.slab + (uint64_t)a.head_off[h];
+    const float *rsc = a.rsc + (uint64_t)slot * a.rstride + (uint64_t)h * dk;
+    const float *csc = a.csc + (uint64_t)slot * a.cstride + (uint64_t)h * dv;
     const int i0 = 4 * (int)(B / (dv >> 2)), j0 = 4 * (int)(B % (dv >> 2));
     const float *S = a.S + nh * (long)dk * dv;
     float z[16];
+    bool nf = false;
 #pragma unroll
     for (int cj = 0; cj < 4; cj++)
 #pragma unroll
         for (int ri = 0; ri < 4; ri++) {
             const float x = S[(long)(i0 + ri) * dv + j0 + cj];
             if constexpr (QUANT) {
-                const float s = a.rsc[(long)h * dk + i0 + ri] * a.csc[(long)h * dv + j0 + cj];
-                // decision on fl32(x / s), ties to even, then the symmetric clamp
-                const float qf = fminf(fmaxf(__builtin_rintf(x / s), 1.0f - OFF), OFF - 1.0f);
+                const float s = rsc[i0 + ri] * csc[j0 + cj];
+                // decision on fl32(x / s), ties to even, then the symmetric
+                // clamp; a NaN quotient becomes code 0, +-Inf the nearest bound
+                const float qt = x / s;
+                nf |= !__builtin_isfinite(qt);
+                const float qf = qt != qt ? 0.0f : fminf(fmaxf(__builtin_rintf(qt), 1.0f - OFF), OFF - 1.0f);
                 z[4 * cj + ri] = qf + OFF;  // integer-valued, exact
             } else {
+                nf |= !__builtin_isfinite(x);
                 z[4 * cj + ri] = x;
             }
         }
+    if (__ballot(nf) && (threadIdx.x & 63) == 0) atomicOr(a.err, 1);
     uint32_t dd[W];
     encode<BITS>(z, dd);
     uint32_t *dst = reinterpret_cast<uint32_t *>(tile + B * 2 * fw<BITS>());
@@ -983,7 +1298,10 @@ __global__ __launch_bounds__(256) void k_load(StepArgs a, float *S, long total_b
     const int n = (int)(tix / a.Hc);
     const int h = a.heads[tix - (long)n * a.Hc];
     const long nh = (long)n * a.H + h;
-    const uint8_t *tile = a.pool + (uint64_t)a.slot_ids[n] * a.slab + (uint64_t)a.head_off[h];
+    const int32_t slot = a.slot_ids[n];
+    const uint8_t *tile = a.pool + (uint64_t)slot * a.slab + (uint64_t)a.head_off[h];
+    const float *rsc = a.rsc + (uint64_t)slot * a.rstride + (uint64_t)h * dk;
+    const float *csc = a.csc + (uint64_t)slot * a.cstride + (uint64_t)h * dv;
     const int i0 = 4 * (int)(B / (dv >> 2)), j0 = 4 * (int)(B % (dv >> 2));
     uint32_t dd[W];
     const uint32_t *src = reinterpret_cast<const uint32_t *>(tile + B * 2 * fw<BITS>());
@@ -998,7 +1316,7 @@ __global__ __launch_bounds__(256) void k_load(StepArgs a, float *S, long total_b
         for (int ri = 0; ri < 4; ri++) {
             float x = f[4 * cj + ri];
             if constexpr (QUANT) {
-                const float s = a.rsc[(long)h * dk + i0 + ri] * a.csc[(long)h * dv + j0 + cj];
+                const float s = rsc[i0 + ri] * csc[j0 + cj];
                 x = (x - OFF) * s;  // the code is exact; one rounding of q * s
             }
             dst[(long)(i0 + ri) * dv + j0 + cj] = x;
@@ -1061,6 +1379,7 @@ hipError_t launch_wide128(Op op, int bits, bool qkv_bf16, const StepArgs &a, int
     if (n_req <= 0 || a.Hc <= 0) return hipSuccess;
     StepArgs b = a;
     b.n_req = n_req;
+    xcd_magic((uint32_t)a.Hc, b.xm);
     const dim3 grid(xcd_grid((uint32_t)n_req, (uint32_t)a.Hc));
     if (bits == 32) {
         if (qkv_bf16) wide128_t<32, uint16_t>(op, b, grid, st);
@@ -1101,6 +1420,7 @@ hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_
     if (n_blocks == 0) return hipSuccess;
     FusedArgs g = f;
     g.a.n_req = (int32_t)(n_blocks / (uint32_t)f.a.H);
+    xcd_magic((uint32_t)f.a.H, g.a.xm);
     const dim3 grid(xcd_grid((uint32_t)g.a.n_req, (uint32_t)f.a.H));
     // two waves per tile, each thread holding eight 4x4 blocks as packed
     // halves, the register budget held to 5 waves per SIMD.  A launch of a
@@ -1137,16 +1457,16 @@ hipError_t launch(Op op, int bits, bool qkv_bf16, const StepArgs &a, int32_t n_r
 
 constexpr int32_t kGenMax = 0x7fffffff;
 
-__global__ __launch_bounds__(256) void k_check_begin(int32_t *flag, int32_t *stamps, int32_t n_slots)
+__global__ __launch_bounds__(256) void k_check_begin(int32_t *flag, int32_t *stamps, int32_t *gen,
+                                                     int32_t n_clear)
 {
-    // stamps[n_slots] is the generation; when it would wrap, every stamp is
-    // zeroed first so that no stale stamp can equal a new generation
+    // when the generation would wrap, stamps[0, n_clear) are zeroed first so
+    // that no stale stamp can equal a new generation
     __shared__ int32_t wrap;
-    int32_t *gen = stamps + n_slots;
     if (threadIdx.x == 0) wrap = gen[0] >= kGenMax;
     __syncthreads();
     if (wrap) {
-        for (int32_t s = threadIdx.x; s < n_slots; s += 256) stamps[s] = 0;
+        for (int32_t s = threadIdx.x; s < n_clear; s += 256) stamps[s] = 0;
         __syncthreads();
     }
     if (threadIdx.x == 0) {
@@ -1156,7 +1476,8 @@ __global__ __launch_bounds__(256) void k_check_begin(int32_t *flag, int32_t *sta
 }
 
 __global__ __launch_bounds__(256) void k_check_slots(const int32_t *ids, int32_t n, int32_t n_slots,
-                                                     int32_t *stamps, int32_t *flag)
+                                                     int32_t *stamps, const int32_t *gen,
+                                                     int32_t *flag)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
@@ -1165,18 +1486,25 @@ __global__ __launch_bounds__(256) void k_check_slots(const int32_t *ids, int32_t
         atomicOr(flag, 1);
         return;
     }
-    const int32_t gen = stamps[n_slots];
-    if (atomicExch(stamps + id, gen) == gen) atomicOr(flag, 2);
+    const int32_t g = gen[0];
+    if (atomicExch(stamps + id, g) == g) atomicOr(flag, 2);
+}
+
+static hipError_t check_slots(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *stamps,
+                              int32_t *gen, int32_t n_clear, int32_t *flag, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_check_begin, dim3(1), dim3(256), 0, st, flag, stamps, gen, n_clear);
+    if (n > 0)
+        hipLaunchKernelGGL(k_check_slots, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids,
+                           n, n_slots, stamps, gen, flag);
+    return hipGetLastError();
 }
 
 hipError_t launch_check_slots(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *stamps,
                               int32_t *flag, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_check_begin, dim3(1), dim3(256), 0, st, flag, stamps, n_slots);
-    if (n > 0)
-        hipLaunchKernelGGL(k_check_slots, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids,
-                           n, n_slots, stamps, flag);
-    return hipGetLastError();
+    // a pool keeps its generation right after its n_slots stamps
+    return check_slots(ids, n, n_slots, stamps, stamps + n_slots, n_slots, flag, st);
 }
 
 }  // namespace sqk

@@ -17,14 +17,17 @@ struct StepArgs {
     int32_t H;                 // heads per request
     int32_t dk, dv;
     const int32_t *slot_ids;   // [n_req]
-    const float *rsc;          // [H][dk]
-    const float *csc;          // [H][dv]
+    const float *rsc;          // row factors of slot p, head h: rsc + p * rstride + h * dk
+    const float *csc;          // column factors: csc + p * cstride + h * dv
+    uint64_t rstride, cstride; // 0 = one set of factors shared by every slot
     const void *q, *k, *v;     // [n_req][H][d]
     const float *alpha;        // [n_req][H]; per-channel gate: [n_req][H][dk]
     const float *beta;         // [n_req][H]
     float *o;                  // [n_req][H][dv] or null
     const float *S;            // store: source, load: destination, [n_req][H][dk][dv]
+    int32_t *err;              // the pool's sticky device flag (bit 0: a non-finite value)
     int32_t n_req;             // requests in the batch (set by the launchers that need it)
+    uint32_t xm[8];            // reciprocals for the XCD-aware tile order (set by the launchers)
 };
 
 // OP_STEP_KDA is the step with a per-key-channel gate (alpha [n_req][H][dk]).

@@ -22,11 +22,12 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM = 0, -1, -2, -3, -4
+SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM, SQ_ERR_DEVICE = 0, -1, -2, -3, -4, -5
 SQ_F32, SQ_BF16 = 0, 1
 EXPORTED = ("sq_pool_bytes", "sq_pool_alloc", "sq_pool_free", "sq_pool_tile_offset",
             "sq_pool_store", "sq_pool_load", "sq_decode_step", "sq_decode_step_kda", "sq_readout",
-            "sq_check_slots", "sq_status_string")
+            "sq_check_slots", "sq_pool_last_device_error",
+            "sq_status_string")
 
 
 class SqPoolDesc(ctypes.Structure):
@@ -34,6 +35,7 @@ class SqPoolDesc(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("head_bits", ctypes.POINTER(ctypes.c_uint8)),
                 ("row_scale", ctypes.c_void_p), ("col_scale", ctypes.c_void_p),
+                ("scale_slot_stride", ctypes.c_int64),
                 ("state", ctypes.c_void_p), ("state_bytes", ctypes.c_uint64)]
 
 
@@ -59,6 +61,8 @@ _lib.sq_readout.restype = ctypes.c_int
 _lib.sq_readout.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp]
 _lib.sq_check_slots.restype = ctypes.c_int
 _lib.sq_check_slots.argtypes = [_vp, _vp, _i32, _vp, _vp]
+_lib.sq_pool_last_device_error.restype = ctypes.c_int
+_lib.sq_pool_last_device_error.argtypes = [_vp, _vp]
 _lib.sq_status_string.restype = ctypes.c_char_p
 _lib.sq_status_string.argtypes = [ctypes.c_int]
 
@@ -139,6 +143,15 @@ def sq_check_slots(pool: SqPool, slot_ids, result, stream=None) -> None:
            "sq_check_slots")
 
 
+def sq_pool_last_device_error(pool: SqPool, stream=None) -> int:
+    """Synchronize the stream, then read and clear the pool's sticky flag:
+    SQ_OK, or SQ_ERR_DEVICE if a kernel met a non-finite updated value."""
+    st = _lib.sq_pool_last_device_error(pool.handle, _stream(stream))
+    if st not in (SQ_OK, SQ_ERR_DEVICE):
+        _check(st, "sq_pool_last_device_error")
+    return st
+
+
 def sq_status_string(status: int) -> str:
     return _lib.sq_status_string(int(status)).decode()
 
@@ -175,17 +188,21 @@ class SqPool:
 
 
 def sq_pool_alloc(n_slots: int, n_heads: int, d_k: int, d_v: int, head_bits, row_scale,
-                  col_scale, state, state_bytes: int | None = None) -> SqPool:
-    """Wrap sq_pool_alloc; `state` is a uint8 device tensor (the caller's buffer)."""
+                  col_scale, state, state_bytes: int | None = None,
+                  scale_slot_stride: int = 0) -> SqPool:
+    """Wrap sq_pool_alloc; `state` is a uint8 device tensor (the caller's buffer).
+    With scale_slot_stride S > 0 the factor tensors hold n_slots * S per-head
+    vectors (slot p, head h at vector p * S + h)."""
     arr, nb = _bits_array(head_bits)
-    _arg(row_scale, "sq_pool_alloc", "row_scale", (torch.float32,), n_heads * d_k)
-    _arg(col_scale, "sq_pool_alloc", "col_scale", (torch.float32,), n_heads * d_v)
+    vecs = n_slots * scale_slot_stride if scale_slot_stride > 0 else n_heads
+    _arg(row_scale, "sq_pool_alloc", "row_scale", (torch.float32,), vecs * d_k)
+    _arg(col_scale, "sq_pool_alloc", "col_scale", (torch.float32,), vecs * d_v)
     if isinstance(state, torch.Tensor):
         _arg(state, "sq_pool_alloc", "state", (state.dtype,), state.numel())
     if state_bytes is None:
         state_bytes = state.numel() * state.element_size() if hasattr(state, "numel") else 0
     desc = SqPoolDesc(n_slots, n_heads, d_k, d_v, arr, _ptr(row_scale), _ptr(col_scale),
-                      _ptr(state), int(state_bytes))
+                      int(scale_slot_stride), _ptr(state), int(state_bytes))
     h = _vp()
     _check(_lib.sq_pool_alloc(ctypes.byref(desc), ctypes.byref(h)), "sq_pool_alloc")
     return SqPool(h.value, (state, row_scale, col_scale), n_slots, n_heads, d_k, d_v,
