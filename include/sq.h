@@ -220,6 +220,25 @@ int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, cons
 int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_t *result,
                    void *stream);
 
+/* The slot check of sq_check_slots for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): it needs no pool, and keeps its per-slot stamps and
+ * generation counter in a fixed array inside the library (one per GPU, about
+ * 256 KB, held until the process ends) instead of a pool's table.  Nothing is
+ * allocated, by this call or by anything it calls.
+ * slot_ids: DEVICE int32 [n_req], checked against [0, n_slots); *result
+ * (DEVICE int32, 4-byte aligned) receives 0, or 1 (an id out of range) | 2
+ * (an id repeated), as for sq_check_slots.  n_slots must be at most
+ * SQ_CHECK_NOALLOC_MAX_SLOTS.  n_req == 0 writes 0.
+ * All calls on one GPU share that GPU's array: calls made on one GPU must not
+ * overlap in time (order them on one stream), or their results race.
+ * Errors: SQ_ERR_INVALID (null result, negative n_req, n_slots < 1, null
+ * slot_ids with n_req > 0, misaligned result), SQ_ERR_UNSUPPORTED (n_slots
+ * above the limit), SQ_ERR_HIP.  Asynchronous on `stream`. */
+#define SQ_CHECK_NOALLOC_MAX_SLOTS 65536
+int sq_check_slots_noalloc(const int32_t *slot_ids, int32_t n_req, int32_t n_slots, int32_t *result,
+                           void *stream);
+
 /* Read and clear the pool's sticky device flag.  The step, the per-channel-
  * gate step and the store set it when an updated value (the quotient S'/s for
  * codes, S' for unquantized heads) is not finite, which only non-finite or

@@ -376,6 +376,19 @@ int sq_check_slots(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, int32_
     return SQ_OK;
 }
 
+int sq_check_slots_noalloc(const int32_t *slot_ids, int32_t n_req, int32_t n_slots, int32_t *result,
+                           void *stream)
+{
+    if (!result || n_req < 0 || n_slots < 1 || (n_req > 0 && !slot_ids) || !aligned(result, 4))
+        return SQ_ERR_INVALID;
+    static_assert(SQ_CHECK_NOALLOC_MAX_SLOTS == sqk::kNoAllocMaxSlots, "one limit");
+    if (n_slots > SQ_CHECK_NOALLOC_MAX_SLOTS) return SQ_ERR_UNSUPPORTED;
+    if (sqk::launch_check_slots_noalloc(slot_ids, n_req, n_slots, result, (hipStream_t)stream) !=
+        hipSuccess)
+        return SQ_ERR_HIP;
+    return SQ_OK;
+}
+
 int sq_pool_last_device_error(sq_pool *pool, void *stream)
 {
     if (!pool) return SQ_ERR_INVALID;

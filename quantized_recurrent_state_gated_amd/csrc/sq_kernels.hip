@@ -30,6 +30,7 @@
 // and the requantization uses alpha_i per row.  Template flag CHG.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 #include <stdint.h>
@@ -1505,6 +1506,44 @@ hipError_t launch_check_slots(const int32_t *ids, int32_t n, int32_t n_slots, in
 {
     // a pool keeps its generation right after its n_slots stamps
     return check_slots(ids, n, n_slots, stamps, stamps + n_slots, n_slots, flag, st);
+}
+
+// ---------------------------------------------------------------- allocation-free slot check
+//
+// The same check with its stamps and generation in a fixed device array of
+// this module instead of a pool's table, for callers that cannot allocate.
+// Each GPU holds its own copy of the array (zero at module load) until the
+// process ends; its address on the current device is looked up once per
+// device with hipGetSymbolAddress, and only that address is handed to the
+// kernels.  Calls on one GPU share the array, so calls that overlap in time
+// on one GPU race.
+
+static __device__ __align__(256) int32_t scratch[kNoAllocMaxSlots + 64];
+
+constexpr int kMaxDevices = 64;
+static int32_t *g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+hipError_t launch_check_slots_noalloc(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *flag,
+                                      hipStream_t st)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int32_t *base;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch[dev]) {
+            void *p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch[dev] = static_cast<int32_t *>(p);
+        }
+        base = g_scratch[dev];
+    }
+    // stamps for every supported slot, then the generation
+    return check_slots(ids, n, n_slots, base, base + kNoAllocMaxSlots, kNoAllocMaxSlots, flag, st);
 }
 
 }  // namespace sqk

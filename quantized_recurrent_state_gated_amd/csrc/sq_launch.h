@@ -61,4 +61,10 @@ hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_
 hipError_t launch_check_slots(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *stamps,
                               int32_t *flag, hipStream_t stream);
 
+// The same check with its stamps in the module's own fixed device array
+// (no allocation); n_slots must be at most kNoAllocMaxSlots.
+constexpr int32_t kNoAllocMaxSlots = 65536;
+hipError_t launch_check_slots_noalloc(const int32_t *ids, int32_t n, int32_t n_slots, int32_t *flag,
+                                      hipStream_t stream);
+
 }  // namespace sqk

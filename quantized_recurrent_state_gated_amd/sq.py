@@ -26,7 +26,7 @@ SQ_OK, SQ_ERR_INVALID, SQ_ERR_UNSUPPORTED, SQ_ERR_HIP, SQ_ERR_NOMEM, SQ_ERR_DEVI
 SQ_F32, SQ_BF16 = 0, 1
 EXPORTED = ("sq_pool_bytes", "sq_pool_alloc", "sq_pool_free", "sq_pool_tile_offset",
             "sq_pool_store", "sq_pool_load", "sq_decode_step", "sq_decode_step_kda", "sq_readout",
-            "sq_check_slots", "sq_pool_last_device_error",
+            "sq_check_slots", "sq_check_slots_noalloc", "sq_pool_last_device_error",
             "sq_status_string")
 
 
@@ -61,6 +61,8 @@ _lib.sq_readout.restype = ctypes.c_int
 _lib.sq_readout.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp]
 _lib.sq_check_slots.restype = ctypes.c_int
 _lib.sq_check_slots.argtypes = [_vp, _vp, _i32, _vp, _vp]
+_lib.sq_check_slots_noalloc.restype = ctypes.c_int
+_lib.sq_check_slots_noalloc.argtypes = [_vp, _i32, _i32, _vp, _vp]
 _lib.sq_pool_last_device_error.restype = ctypes.c_int
 _lib.sq_pool_last_device_error.argtypes = [_vp, _vp]
 _lib.sq_status_string.restype = ctypes.c_char_p
@@ -141,6 +143,15 @@ def sq_check_slots(pool: SqPool, slot_ids, result, stream=None) -> None:
     _arg(result, "sq_check_slots", "result", (torch.int32,), 1)
     _check(_lib.sq_check_slots(pool.handle, _ptr(slot_ids), n_req, _ptr(result), _stream(stream)),
            "sq_check_slots")
+
+
+def sq_check_slots_noalloc(slot_ids, n_slots: int, result, stream=None) -> None:
+    """sq_check_slots without a pool and without any allocation: the stamps
+    live in a fixed array inside the library (n_slots <= SQ_CHECK_NOALLOC_MAX_SLOTS)."""
+    n_req = 0 if slot_ids is None else int(slot_ids.numel())
+    _arg(result, "sq_check_slots_noalloc", "result", (torch.int32,), 1)
+    _check(_lib.sq_check_slots_noalloc(_ptr(slot_ids), n_req, int(n_slots), _ptr(result),
+                                       _stream(stream)), "sq_check_slots_noalloc")
 
 
 def sq_pool_last_device_error(pool: SqPool, stream=None) -> int:
