@@ -65,24 +65,25 @@ def _load():
         "orc_quantize": (ctypes.c_int, [ctypes.c_int, ctypes.c_double, ctypes.c_double]),
         "orc_encode_field": (ctypes.c_uint32, [ctypes.c_int, ctypes.c_double, ctypes.c_double]),
         "orc_decode_tile": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p, _f64p]),
-        "orc_encode_tile": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f32p, _f32p, _u8p]),
-        "orc_step_tile": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
+        "orc_nonfinite_field": (ctypes.c_int, [ctypes.c_int, ctypes.c_double, ctypes.c_double]),
+        "orc_encode_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f32p, _f32p, _u8p]),
+        "orc_step_tile": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
                                  _f32p, _f32p, _f32p, ctypes.c_float, ctypes.c_float, _f32p]),
         "orc_readout_tile": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
                                     _f32p, _f32p]),
-        "orc_step_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
-                                 _i32p, ctypes.c_int, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+        "orc_step_pool": (ctypes.c_long, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
+                                          _f32p, ctypes.c_long, _i32p, ctypes.c_int, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
                                  ctypes.c_int]),
         "orc_readout_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
-                                    _f32p, _i32p, ctypes.c_int, _f32p, _f32p, ctypes.c_int]),
-        "orc_store_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
-                                  _f32p, _i32p, ctypes.c_int, _f32p]),
+                                    _f32p, ctypes.c_long, _i32p, ctypes.c_int, _f32p, _f32p, ctypes.c_int]),
+        "orc_store_pool": (ctypes.c_long, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p,
+                                           _f32p, _f32p, ctypes.c_long, _i32p, ctypes.c_int, _f32p]),
         "orc_load_pool": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
-                                 _f32p, _i32p, ctypes.c_int, _f32p]),
-        "orc_step_tile_kda": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
+                                 _f32p, ctypes.c_long, _i32p, ctypes.c_int, _f32p]),
+        "orc_step_tile_kda": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p, _f32p,
                                      _f32p, _f32p, _f32p, _f32p, ctypes.c_float, _f32p]),
-        "orc_step_pool_kda": (None, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, _f32p,
-                                     _f32p, _i32p, ctypes.c_int, _f32p, _f32p, _f32p, _f32p, _f32p,
+        "orc_step_pool_kda": (ctypes.c_long, [_u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p,
+                                              _f32p, _f32p, ctypes.c_long, _i32p, ctypes.c_int, _f32p, _f32p, _f32p, _f32p, _f32p,
                                      _f32p, ctypes.c_int]),
         "orc_bruteforce_kda": (None, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p, _f64p,
                                       _f64p, _f64p, _f64p, _f64p, _f64p]),
@@ -184,6 +185,11 @@ def decode_field(bits: int, f: int, s: float) -> float:
     return float(_load().orc_decode_field(bits, f, s))
 
 
+def nonfinite_field(bits: int, x: float, s: float) -> bool:
+    """Is the value a field is decided on (fl32(x/s) for a code, fl32(x) else) not finite?"""
+    return bool(_load().orc_nonfinite_field(bits, x, s))
+
+
 # ---------------------------------------------------------------- tiles
 
 def decode_tile(bits: int, dk: int, dv: int, tile, r, c) -> np.ndarray:
@@ -194,23 +200,28 @@ def decode_tile(bits: int, dk: int, dv: int, tile, r, c) -> np.ndarray:
     return S
 
 
-def encode_tile(bits: int, dk: int, dv: int, S, r, c) -> np.ndarray:
+def encode_tile(bits: int, dk: int, dv: int, S, r, c, return_flag: bool = False):
+    """Packed tile of S; with return_flag, (tile, whether a stored-from value was non-finite)."""
     S = _c(S, np.float64)
     r, c = _c(r, np.float32), _c(c, np.float32)
     tile = np.zeros(tile_bytes(bits, dk, dv), np.uint8)
-    _load().orc_encode_tile(bits, dk, dv, _p(S, _f64p), _p(r, _f32p), _p(c, _f32p), _p(tile, _u8p))
-    return tile
+    bad = _load().orc_encode_tile(bits, dk, dv, _p(S, _f64p), _p(r, _f32p), _p(c, _f32p),
+                                  _p(tile, _u8p))
+    return (tile, bool(bad)) if return_flag else tile
 
 
-def step_tile(bits: int, dk: int, dv: int, tile, r, c, q, k, v, alpha: float, beta: float):
-    """Return (new tile bytes, o float32[dv]); the input tile is not modified."""
+def step_tile(bits: int, dk: int, dv: int, tile, r, c, q, k, v, alpha: float, beta: float,
+              return_flag: bool = False):
+    """Return (new tile bytes, o float32[dv]) and, with return_flag, whether the step
+    met a non-finite value; the input tile is not modified."""
     tile = _c(tile, np.uint8).copy()
     r, c = _c(r, np.float32), _c(c, np.float32)
     q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
     o = np.empty(dv, np.float32)
-    _load().orc_step_tile(bits, dk, dv, _p(tile, _u8p), _p(r, _f32p), _p(c, _f32p), _p(q, _f32p),
-                          _p(k, _f32p), _p(v, _f32p), float(alpha), float(beta), _p(o, _f32p))
-    return tile, o
+    bad = _load().orc_step_tile(bits, dk, dv, _p(tile, _u8p), _p(r, _f32p), _p(c, _f32p),
+                                _p(q, _f32p), _p(k, _f32p), _p(v, _f32p), float(alpha),
+                                float(beta), _p(o, _f32p))
+    return (tile, o, bool(bad)) if return_flag else (tile, o)
 
 
 def readout_tile(bits: int, dk: int, dv: int, tile, r, c, q) -> np.ndarray:
@@ -230,9 +241,25 @@ def _threads(n_threads):
     return int(n_threads)
 
 
+def _check_factors(r, c, H, dk, dv, sid, scale_stride):
+    """Factors of slot p, head h sit at r[(p*S + h)*dk] (S = scale_stride; 0 = shared)."""
+    S = int(scale_stride)
+    assert S == 0 or S >= H
+    top = 0 if (S == 0 or sid.size == 0) else int(sid.max()) * S
+    assert r.size >= (top + H) * dk and c.size >= (top + H) * dv
+    return S
+
+
+def _check_slots(hb, dk, dv, sid, pool):
+    _, slab = pool_layout(hb, dk, dv)
+    assert sid.size == 0 or (sid.min() >= 0 and (int(sid.max()) + 1) * slab <= pool.size)
+
+
 def step_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, q, k, v, alpha, beta,
-              want_o: bool = True, n_threads=None):
-    """Advance the pool in place by one step; return o float32[n_req][H][dv] (or None)."""
+              want_o: bool = True, n_threads=None, scale_stride: int = 0,
+              return_flagged: bool = False):
+    """Advance the pool in place by one step; return o float32[n_req][H][dv] (or None),
+    and with return_flagged also the number of tiles that met a non-finite value."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
     hb = _c(head_bits, np.uint8)
     H = hb.size
@@ -243,50 +270,60 @@ def step_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, q, 
     alpha, beta = _c(alpha, np.float32), _c(beta, np.float32)
     assert q.size == n_req * H * dk and k.size == n_req * H * dk and v.size == n_req * H * dv
     assert alpha.size == n_req * H and beta.size == n_req * H
-    assert r.size == H * dk and c.size == H * dv
-    _, slab = pool_layout(hb, dk, dv)
-    assert n_req == 0 or (sid.min() >= 0 and (int(sid.max()) + 1) * slab <= pool.size)
+    S = _check_factors(r, c, H, dk, dv, sid, scale_stride)
+    _check_slots(hb, dk, dv, sid, pool)
     o = np.empty((n_req, H, dv), np.float32) if want_o else None
-    _load().orc_step_pool(_p(pool, _u8p), H, dk, dv, _p(hb, _u8p), _p(r, _f32p), _p(c, _f32p),
-                          _p(sid, _i32p), n_req, _p(q, _f32p), _p(k, _f32p), _p(v, _f32p),
-                          _p(alpha, _f32p), _p(beta, _f32p),
-                          _p(o, _f32p) if want_o else None, _threads(n_threads))
-    return o
+    bad = _load().orc_step_pool(_p(pool, _u8p), H, dk, dv, _p(hb, _u8p), _p(r, _f32p),
+                                _p(c, _f32p), S, _p(sid, _i32p), n_req, _p(q, _f32p),
+                                _p(k, _f32p), _p(v, _f32p), _p(alpha, _f32p), _p(beta, _f32p),
+                                _p(o, _f32p) if want_o else None, _threads(n_threads))
+    return (o, int(bad)) if return_flagged else o
 
 
-def readout_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, q, n_threads=None):
+def readout_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, q, n_threads=None,
+                 scale_stride: int = 0):
     pool = _c(pool, np.uint8)
     hb = _c(head_bits, np.uint8)
     H = hb.size
     sid = _c(slot_ids, np.int32)
     n_req = sid.size
     r, c, q = _c(r, np.float32), _c(c, np.float32), _c(q, np.float32)
+    S = _check_factors(r, c, H, dk, dv, sid, scale_stride)
+    _check_slots(hb, dk, dv, sid, pool)
     o = np.empty((n_req, H, dv), np.float32)
     _load().orc_readout_pool(_p(pool, _u8p), H, dk, dv, _p(hb, _u8p), _p(r, _f32p), _p(c, _f32p),
-                             _p(sid, _i32p), n_req, _p(q, _f32p), _p(o, _f32p), _threads(n_threads))
+                             S, _p(sid, _i32p), n_req, _p(q, _f32p), _p(o, _f32p),
+                             _threads(n_threads))
     return o
 
 
-def store_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, S) -> None:
-    """Quantize fp32 states S[n_req][H][dk][dv] into the slots' tiles (in place)."""
+def store_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, S,
+               scale_stride: int = 0) -> int:
+    """Quantize fp32 states S[n_req][H][dk][dv] into the slots' tiles (in place);
+    return the number of tiles that stored a value from a non-finite one."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
     hb = _c(head_bits, np.uint8)
     sid = _c(slot_ids, np.int32)
     r, c, S = _c(r, np.float32), _c(c, np.float32), _c(S, np.float32)
     assert S.size == sid.size * hb.size * dk * dv
-    _load().orc_store_pool(_p(pool, _u8p), hb.size, dk, dv, _p(hb, _u8p), _p(r, _f32p),
-                           _p(c, _f32p), _p(sid, _i32p), sid.size, _p(S, _f32p))
+    st = _check_factors(r, c, hb.size, dk, dv, sid, scale_stride)
+    _check_slots(hb, dk, dv, sid, pool)
+    return int(_load().orc_store_pool(_p(pool, _u8p), hb.size, dk, dv, _p(hb, _u8p), _p(r, _f32p),
+                                      _p(c, _f32p), st, _p(sid, _i32p), sid.size, _p(S, _f32p)))
 
 
-def load_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids) -> np.ndarray:
+def load_pool(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids,
+              scale_stride: int = 0) -> np.ndarray:
     """Decoded fp32 states S[n_req][H][dk][dv] of the slots' tiles."""
     pool = _c(pool, np.uint8)
     hb = _c(head_bits, np.uint8)
     sid = _c(slot_ids, np.int32)
     r, c = _c(r, np.float32), _c(c, np.float32)
+    st = _check_factors(r, c, hb.size, dk, dv, sid, scale_stride)
+    _check_slots(hb, dk, dv, sid, pool)
     S = np.empty((sid.size, hb.size, dk, dv), np.float32)
     _load().orc_load_pool(_p(pool, _u8p), hb.size, dk, dv, _p(hb, _u8p), _p(r, _f32p),
-                          _p(c, _f32p), _p(sid, _i32p), sid.size, _p(S, _f32p))
+                          _p(c, _f32p), st, _p(sid, _i32p), sid.size, _p(S, _f32p))
     return S
 
 
@@ -306,21 +343,24 @@ def bruteforce(S0, q, k, v, alpha, beta):
 
 # ---------------------------------------------------------------- per-channel gate
 
-def step_tile_kda(bits: int, dk: int, dv: int, tile, r, c, q, k, v, alpha, beta: float):
-    """Per-channel-gate step (alpha float32[dk]); returns (new tile, o)."""
+def step_tile_kda(bits: int, dk: int, dv: int, tile, r, c, q, k, v, alpha, beta: float,
+                  return_flag: bool = False):
+    """Per-channel-gate step (alpha float32[dk]); returns (new tile, o) [, flag]."""
     tile = _c(tile, np.uint8).copy()
     r, c = _c(r, np.float32), _c(c, np.float32)
     q, k, v, a = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32), _c(alpha, np.float32)
     o = np.empty(dv, np.float32)
-    _load().orc_step_tile_kda(bits, dk, dv, _p(tile, _u8p), _p(r, _f32p), _p(c, _f32p),
-                              _p(q, _f32p), _p(k, _f32p), _p(v, _f32p), _p(a, _f32p), float(beta),
-                              _p(o, _f32p))
-    return tile, o
+    bad = _load().orc_step_tile_kda(bits, dk, dv, _p(tile, _u8p), _p(r, _f32p), _p(c, _f32p),
+                                    _p(q, _f32p), _p(k, _f32p), _p(v, _f32p), _p(a, _f32p),
+                                    float(beta), _p(o, _f32p))
+    return (tile, o, bool(bad)) if return_flag else (tile, o)
 
 
 def step_pool_kda(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids, q, k, v, alpha,
-                  beta, want_o: bool = True, n_threads=None):
-    """Per-channel-gate pool step in place (alpha float32 [n_req][H][dk]); returns o or None."""
+                  beta, want_o: bool = True, n_threads=None, scale_stride: int = 0,
+                  return_flagged: bool = False):
+    """Per-channel-gate pool step in place (alpha float32 [n_req][H][dk]); returns o or
+    None, and with return_flagged also the number of tiles that met a non-finite value."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
     hb = _c(head_bits, np.uint8)
     H = hb.size
@@ -331,15 +371,14 @@ def step_pool_kda(pool: np.ndarray, head_bits, dk: int, dv: int, r, c, slot_ids,
     alpha, beta = _c(alpha, np.float32), _c(beta, np.float32)
     assert q.size == n_req * H * dk and k.size == n_req * H * dk and v.size == n_req * H * dv
     assert alpha.size == n_req * H * dk and beta.size == n_req * H
-    assert r.size == H * dk and c.size == H * dv
-    _, slab = pool_layout(hb, dk, dv)
-    assert n_req == 0 or (sid.min() >= 0 and (int(sid.max()) + 1) * slab <= pool.size)
+    S = _check_factors(r, c, H, dk, dv, sid, scale_stride)
+    _check_slots(hb, dk, dv, sid, pool)
     o = np.empty((n_req, H, dv), np.float32) if want_o else None
-    _load().orc_step_pool_kda(_p(pool, _u8p), H, dk, dv, _p(hb, _u8p), _p(r, _f32p), _p(c, _f32p),
-                              _p(sid, _i32p), n_req, _p(q, _f32p), _p(k, _f32p), _p(v, _f32p),
-                              _p(alpha, _f32p), _p(beta, _f32p),
-                              _p(o, _f32p) if want_o else None, _threads(n_threads))
-    return o
+    bad = _load().orc_step_pool_kda(_p(pool, _u8p), H, dk, dv, _p(hb, _u8p), _p(r, _f32p),
+                                    _p(c, _f32p), S, _p(sid, _i32p), n_req, _p(q, _f32p),
+                                    _p(k, _f32p), _p(v, _f32p), _p(alpha, _f32p), _p(beta, _f32p),
+                                    _p(o, _f32p) if want_o else None, _threads(n_threads))
+    return (o, int(bad)) if return_flagged else o
 
 
 def bruteforce_kda(S0, q, k, v, alpha, beta):

@@ -285,17 +285,33 @@ void orc_decode_tile(int bits, int dk, int dv, const uint8_t *tile, const float 
         }
 }
 
-/* Encode an fp64 tile (row-major) into packed fields. */
-void orc_encode_tile(int bits, int dk, int dv, const double *S, const float *r, const float *c,
-                     uint8_t *tile)
+/* Is the value an element is stored from not finite?  For a code that value
+ * is the fp32 quotient fl32(x / s) the code is decided on; for an FP16, BF16
+ * or FP32 element it is fl32(x).  (The pages are silent on non-finite values;
+ * the reading taken is that the store reports them, see orc_encode_tile.) */
+int orc_nonfinite_field(int bits, double x, double s)
+{
+    float y = (bits == 4 || bits == 6 || bits == 8) ? (float)(x / s) : (float)x;
+    return !isfinite(y);
+}
+
+/* Encode an fp64 tile (row-major) into packed fields.  Returns 1 if any
+ * element's stored-from value is not finite (orc_nonfinite_field), else 0:
+ * the tile's contribution to the pool's sticky flag.  Such an element is still
+ * stored by the rule of orc_quantize / the float conversions. */
+int orc_encode_tile(int bits, int dk, int dv, const double *S, const float *r, const float *c,
+                    uint8_t *tile)
 {
     int w = orc_field_width(bits);
+    int bad = 0;
     for (int i = 0; i < dk; i++)
         for (int j = 0; j < dv; j++) {
             double s = (bits <= 8) ? orc_step_size(r[i], c[j]) : 1.0;
-            orc_field_put(tile, w, orc_elem_index(i, j, dv),
-                          orc_encode_field(bits, S[(long)i * dv + j], s));
+            double x = S[(long)i * dv + j];
+            bad |= orc_nonfinite_field(bits, x, s);
+            orc_field_put(tile, w, orc_elem_index(i, j, dv), orc_encode_field(bits, x, s));
         }
+    return bad;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -314,9 +330,9 @@ void orc_encode_tile(int bits, int dk, int dv, const double *S, const float *r, 
 /* over rows) is taken from the updated state before requantization.         */
 /* ------------------------------------------------------------------------ */
 
-void orc_step_tile(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
-                   const float *q, const float *k, const float *v, float alpha, float beta,
-                   float *o)
+int orc_step_tile(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
+                  const float *q, const float *k, const float *v, float alpha, float beta,
+                  float *o)
 {
     double *S = (double *)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
     double *u = (double *)malloc(sizeof(double) * (size_t)dv);
@@ -337,9 +353,10 @@ void orc_step_tile(int bits, int dk, int dv, uint8_t *tile, const float *r, cons
             o[j] = (float)acc;
         }
     }
-    orc_encode_tile(bits, dk, dv, S, r, c, tile);
+    int bad = orc_encode_tile(bits, dk, dv, S, r, c, tile);
     free(u);
     free(S);
+    return bad;
 }
 
 /* Readout without update: o = S^T q from the stored (dequantized) state. */
@@ -359,9 +376,14 @@ void orc_readout_tile(int bits, int dk, int dv, const uint8_t *tile, const float
 /* ------------------------------------------------------------------------ */
 /* Pool-level step: the batch of requests n = 0..n_req-1, request n owning  */
 /* slot slot_ids[n].  Inputs are row-major [n_req][H][d]; alpha, beta are    */
-/* [n_req][H]; scales r [H][d_k], c [H][d_v] are shared by all slots.  The   */
+/* [n_req][H].  The factors of slot p, head h are r + (p*S + h)*d_k and      */
+/* c + (p*S + h)*d_v: with the scale stride S = 0 one set [H][d] is shared   */
+/* by every slot, with S >= H every slot has its own ([P5] 空间维度 gives     */
+/* each row and each column of a state matrix its own factor).  The          */
 /* (request, head) tiles are independent; they are split over n_threads     */
-/* plain threads in contiguous chunks.                                        */
+/* plain threads in contiguous chunks.  The step returns how many tiles     */
+/* stored a value from a non-finite one (orc_encode_tile): the pool's       */
+/* sticky flag is set iff that count is non-zero.                            */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -371,17 +393,24 @@ typedef struct {
     int n_heads, dk, dv;
     const uint8_t *bits;
     const float *r, *c;
+    long sstride; /* scale slot stride S */
     const int32_t *slot_ids;
     const float *q, *k, *v, *alpha, *beta;
     float *o;
     long t0, t1;
     int readout_only;
     int channel_gate; /* alpha is [n_req][H][d_k] (orc_step_tile_kda) */
+    long flagged;     /* out: tiles whose step met a non-finite value */
 } orc_job;
 
-void orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
-                       const float *q, const float *k, const float *v, const float *alpha,
-                       float beta, float *o);
+static const float *orc_factors(const float *base, long stride, int32_t slot, int h, int d)
+{
+    return base + ((long)slot * stride + h) * (long)d;
+}
+
+int orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
+                      const float *q, const float *k, const float *v, const float *alpha,
+                      float beta, float *o);
 
 static void *orc_worker(void *arg)
 {
@@ -390,36 +419,38 @@ static void *orc_worker(void *arg)
         long n = t / J->n_heads;
         int h = (int)(t % J->n_heads);
         uint8_t *tile = J->pool + (long)J->slot_ids[n] * J->slab + J->off[h];
-        const float *r = J->r + (long)h * J->dk;
-        const float *c = J->c + (long)h * J->dv;
+        const float *r = orc_factors(J->r, J->sstride, J->slot_ids[n], h, J->dk);
+        const float *c = orc_factors(J->c, J->sstride, J->slot_ids[n], h, J->dv);
         const float *q = J->q + t * J->dk;
         float *o = J->o ? J->o + t * J->dv : NULL;
         if (J->readout_only) {
             orc_readout_tile(J->bits[h], J->dk, J->dv, tile, r, c, q, o);
         } else if (J->channel_gate) {
-            orc_step_tile_kda(J->bits[h], J->dk, J->dv, tile, r, c, q, J->k + t * J->dk,
-                              J->v + t * J->dv, J->alpha + t * J->dk, J->beta[t], o);
+            J->flagged += orc_step_tile_kda(J->bits[h], J->dk, J->dv, tile, r, c, q,
+                                            J->k + t * J->dk, J->v + t * J->dv,
+                                            J->alpha + t * J->dk, J->beta[t], o);
         } else {
-            orc_step_tile(J->bits[h], J->dk, J->dv, tile, r, c, q, J->k + t * J->dk,
-                          J->v + t * J->dv, J->alpha[t], J->beta[t], o);
+            J->flagged += orc_step_tile(J->bits[h], J->dk, J->dv, tile, r, c, q, J->k + t * J->dk,
+                                        J->v + t * J->dv, J->alpha[t], J->beta[t], o);
         }
     }
     return NULL;
 }
 
-static void orc_run(orc_job *base, long n_tiles, int n_threads)
+static long orc_run(orc_job *base, long n_tiles, int n_threads)
 {
     if (n_threads < 1) n_threads = 1;
     if (n_threads > 256) n_threads = 256;
     pthread_t th[256];
     orc_job jobs[256];
     long chunk = (n_tiles + n_threads - 1) / n_threads;
-    int started = 0;
+    int started = 0, n_jobs = 0;
     for (int w = 0; w < n_threads; w++) {
         jobs[w] = *base;
         jobs[w].t0 = (long)w * chunk;
         jobs[w].t1 = jobs[w].t0 + chunk < n_tiles ? jobs[w].t0 + chunk : n_tiles;
         if (jobs[w].t0 >= jobs[w].t1) break;
+        n_jobs++;
         if (n_threads == 1) {
             orc_worker(&jobs[w]);
         } else {
@@ -428,11 +459,14 @@ static void orc_run(orc_job *base, long n_tiles, int n_threads)
         }
     }
     for (int w = 0; w < started; w++) pthread_join(th[w], NULL);
+    long flagged = 0;
+    for (int w = 0; w < n_jobs; w++) flagged += jobs[w].flagged;
+    return flagged;
 }
 
-void orc_step_pool(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
-                   const float *r, const float *c, const int32_t *slot_ids, int n_req,
-                   const float *q, const float *k, const float *v, const float *alpha,
+long orc_step_pool(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
+                   const float *r, const float *c, long scale_stride, const int32_t *slot_ids,
+                   int n_req, const float *q, const float *k, const float *v, const float *alpha,
                    const float *beta, float *o, int n_threads)
 {
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
@@ -447,6 +481,7 @@ void orc_step_pool(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *he
     J.bits = head_bits;
     J.r = r;
     J.c = c;
+    J.sstride = scale_stride;
     J.slot_ids = slot_ids;
     J.q = q;
     J.k = k;
@@ -454,13 +489,14 @@ void orc_step_pool(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *he
     J.alpha = alpha;
     J.beta = beta;
     J.o = o;
-    orc_run(&J, (long)n_req * n_heads, n_threads);
+    long flagged = orc_run(&J, (long)n_req * n_heads, n_threads);
     free(off);
+    return flagged;
 }
 
 void orc_readout_pool(const uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
-                      const float *r, const float *c, const int32_t *slot_ids, int n_req,
-                      const float *q, float *o, int n_threads)
+                      const float *r, const float *c, long scale_stride, const int32_t *slot_ids,
+                      int n_req, const float *q, float *o, int n_threads)
 {
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
     orc_job J;
@@ -474,6 +510,7 @@ void orc_readout_pool(const uint8_t *pool, int n_heads, int dk, int dv, const ui
     J.bits = head_bits;
     J.r = r;
     J.c = c;
+    J.sstride = scale_stride;
     J.slot_ids = slot_ids;
     J.q = q;
     J.o = o;
@@ -483,23 +520,28 @@ void orc_readout_pool(const uint8_t *pool, int n_heads, int dk, int dv, const ui
 }
 
 /* Quantize-and-store: encode fp32 states S[n_req][H][d_k][d_v] (row-major)
- * into the tiles of slots slot_ids[n]. */
-void orc_store_pool(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
-                    const float *r, const float *c, const int32_t *slot_ids, int n_req,
-                    const float *S)
+ * into the tiles of slots slot_ids[n], factors as orc_step_pool.  Returns the
+ * number of tiles that stored a value from a non-finite one. */
+long orc_store_pool(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
+                    const float *r, const float *c, long scale_stride, const int32_t *slot_ids,
+                    int n_req, const float *S)
 {
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
     long slab = orc_pool_layout(n_heads, head_bits, dk, dv, off);
     double *D = (double *)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+    long flagged = 0;
     for (int n = 0; n < n_req; n++)
         for (int h = 0; h < n_heads; h++) {
             const float *src = S + ((long)n * n_heads + h) * (long)dk * dv;
             for (long e = 0; e < (long)dk * dv; e++) D[e] = (double)src[e];
-            orc_encode_tile(head_bits[h], dk, dv, D, r + (long)h * dk, c + (long)h * dv,
-                            pool + (long)slot_ids[n] * slab + off[h]);
+            flagged += orc_encode_tile(head_bits[h], dk, dv, D,
+                                       orc_factors(r, scale_stride, slot_ids[n], h, dk),
+                                       orc_factors(c, scale_stride, slot_ids[n], h, dv),
+                                       pool + (long)slot_ids[n] * slab + off[h]);
         }
     free(D);
     free(off);
+    return flagged;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -602,7 +644,8 @@ void orc_f16_to_f32_array(const uint16_t *h, float *x, long n)
  * once to fp32 (codes: fl32(q * s_ij); pivots: the binary16 value; FP32: the
  * stored value). */
 void orc_load_pool(const uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
-                   const float *r, const float *c, const int32_t *slot_ids, int n_req, float *S)
+                   const float *r, const float *c, long scale_stride, const int32_t *slot_ids,
+                   int n_req, float *S)
 {
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
     long slab = orc_pool_layout(n_heads, head_bits, dk, dv, off);
@@ -610,7 +653,8 @@ void orc_load_pool(const uint8_t *pool, int n_heads, int dk, int dv, const uint8
     for (int n = 0; n < n_req; n++)
         for (int h = 0; h < n_heads; h++) {
             orc_decode_tile(head_bits[h], dk, dv, pool + (long)slot_ids[n] * slab + off[h],
-                            r + (long)h * dk, c + (long)h * dv, D);
+                            orc_factors(r, scale_stride, slot_ids[n], h, dk),
+                            orc_factors(c, scale_stride, slot_ids[n], h, dv), D);
             float *dst = S + ((long)n * n_heads + h) * (long)dk * dv;
             for (long e = 0; e < (long)dk * dv; e++) dst[e] = (float)D[e];
         }
@@ -627,9 +671,9 @@ void orc_load_pool(const uint8_t *pool, int n_heads, int dk, int dv, const uint8
 /*     + beta k_i (v_j - u_j),  o = S'^T q.                                  */
 /* ------------------------------------------------------------------------ */
 
-void orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
-                       const float *q, const float *k, const float *v, const float *alpha,
-                       float beta, float *o)
+int orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, const float *c,
+                      const float *q, const float *k, const float *v, const float *alpha,
+                      float beta, float *o)
 {
     double *S = (double *)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
     double *u = (double *)malloc(sizeof(double) * (size_t)dv);
@@ -651,17 +695,18 @@ void orc_step_tile_kda(int bits, int dk, int dv, uint8_t *tile, const float *r, 
             o[j] = (float)acc;
         }
     }
-    orc_encode_tile(bits, dk, dv, S, r, c, tile);
+    int bad = orc_encode_tile(bits, dk, dv, S, r, c, tile);
     free(u);
     free(S);
+    return bad;
 }
 
 /* Pool-level per-channel-gate step; alpha is [n_req][H][d_k], the rest as
  * orc_step_pool. */
-void orc_step_pool_kda(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
-                       const float *r, const float *c, const int32_t *slot_ids, int n_req,
-                       const float *q, const float *k, const float *v, const float *alpha,
-                       const float *beta, float *o, int n_threads)
+long orc_step_pool_kda(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t *head_bits,
+                       const float *r, const float *c, long scale_stride, const int32_t *slot_ids,
+                       int n_req, const float *q, const float *k, const float *v,
+                       const float *alpha, const float *beta, float *o, int n_threads)
 {
     int64_t *off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_heads > 0 ? n_heads : 1));
     orc_job J;
@@ -675,6 +720,7 @@ void orc_step_pool_kda(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t
     J.bits = head_bits;
     J.r = r;
     J.c = c;
+    J.sstride = scale_stride;
     J.slot_ids = slot_ids;
     J.q = q;
     J.k = k;
@@ -683,8 +729,9 @@ void orc_step_pool_kda(uint8_t *pool, int n_heads, int dk, int dv, const uint8_t
     J.beta = beta;
     J.o = o;
     J.channel_gate = 1;
-    orc_run(&J, (long)n_req * n_heads, n_threads);
+    long flagged = orc_run(&J, (long)n_req * n_heads, n_threads);
     free(off);
+    return flagged;
 }
 
 /* Dense fp64 recurrence with A_t = (I - beta_t k_t k_t^T) diag(alpha_t);

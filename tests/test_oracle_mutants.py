@@ -31,8 +31,8 @@ MUTANTS = [
      "for (int i = 0; i < dk; i++) acc += (double)k[i] * S[(long)i * dv + j];\n        u[j] = acc;\n    }\n    double a = alpha",
      "for (int i = 0; i < dk; i++) acc += (double)k[i] * S[(long)(i % dv) * dv + (j % dk)];\n        u[j] = acc;\n    }\n    double a = alpha"),
     ("readout with the key instead of the query",
-     "            for (int i = 0; i < dk; i++) acc += (double)q[i] * S[(long)i * dv + j];\n            o[j] = (float)acc;\n        }\n    }\n    orc_encode_tile(bits, dk, dv, S, r, c, tile);\n    free(u);\n    free(S);\n}\n\n/* Readout without update",
-     "            for (int i = 0; i < dk; i++) acc += (double)k[i] * S[(long)i * dv + j];\n            o[j] = (float)acc;\n        }\n    }\n    orc_encode_tile(bits, dk, dv, S, r, c, tile);\n    free(u);\n    free(S);\n}\n\n/* Readout without update"),
+     "            for (int i = 0; i < dk; i++) acc += (double)q[i] * S[(long)i * dv + j];\n            o[j] = (float)acc;\n        }\n    }\n    int bad = orc_encode_tile(bits, dk, dv, S, r, c, tile);\n    free(u);\n    free(S);\n    return bad;\n}\n\n/* Readout without update",
+     "            for (int i = 0; i < dk; i++) acc += (double)k[i] * S[(long)i * dv + j];\n            o[j] = (float)acc;\n        }\n    }\n    int bad = orc_encode_tile(bits, dk, dv, S, r, c, tile);\n    free(u);\n    free(S);\n    return bad;\n}\n\n/* Readout without update"),
     ("rounding: ties away from zero instead of to even",
      "if (frac > 0.5) return fl + 1.0;", "if (frac >= 0.5) return fl + 1.0;"),
     ("range: saturation one code too wide",
@@ -57,6 +57,12 @@ MUTANTS = [
      "*= (double)alpha[i]; /* T */", "*= (double)alpha[dk - 1 - i]; /* T */"),
     ("bfloat16: one mantissa bit too many",
      "double ulp = ldexp(1.0, ex - 7);", "double ulp = ldexp(1.0, ex - 8);"),
+    ("per-slot factors: the slot's own set ignored",
+     "return base + ((long)slot * stride + h) * (long)d;", "return base + (long)h * (long)d;"),
+    ("non-finite report: taken on the value, not on the quotient a code is decided on",
+     "? (float)(x / s) : (float)x;", "? (float)x : (float)x;"),
+    ("non-finite report: never raised",
+     "bad |= orc_nonfinite_field(bits, x, s);", "bad |= 0 * orc_nonfinite_field(bits, x, s);"),
 ]
 
 

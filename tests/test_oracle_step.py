@@ -513,3 +513,150 @@ def test_kda_pool_matches_tiles_and_threads(orc):
         o = orc.step_pool_kda(got, bits, dk, dv, r, c, slots, q, k, v, a, b, n_threads=threads)
         assert np.array_equal(got, want)
         assert np.array_equal(o, o_want)
+
+
+def test_per_slot_factors_follow_the_slot(orc):
+    """With a scale stride S every slot p has its own factors at (p*S + h); a
+    stored code decodes to code * fl32(r_pi c_pj) of its own slot (checked in
+    numpy), and the pool calls equal the tile calls on the slot's factors."""
+    rng = np.random.default_rng(93)
+    dk, dv = 16, 12
+    bits = np.array([4, 6, 8, 16, 32], np.uint8)
+    H, S = bits.size, bits.size + 2
+    n_slots = 4
+    off, slab = orc.pool_layout(bits, dk, dv)
+    pool = np.zeros(n_slots * slab, np.uint8)
+    r = _f32(rng.uniform(0.5, 2.0, (n_slots * S, dk)))
+    c = _f32(rng.uniform(0.01, 0.05, (n_slots * S, dv)))
+    slots = np.array([3, 1], np.int32)
+    X = np.empty((slots.size, H, dk, dv), np.float32)
+    codes = {}
+    for n, p in enumerate(slots):
+        for h in range(H):
+            b = int(bits[h])
+            if b <= 8:
+                Q = 2 ** (b - 1) - 1
+                codes[n, h] = rng.integers(-Q, Q + 1, (dk, dv))
+                s = (r[p * S + h][:, None].astype(np.float64) * c[p * S + h][None, :]).astype(np.float32)
+                X[n, h] = codes[n, h] * s.astype(np.float64)
+            else:
+                X[n, h] = rng.standard_normal((dk, dv))
+    assert orc.store_pool(pool, bits, dk, dv, r, c, slots, X, scale_stride=S) == 0
+    L = orc.load_pool(pool, bits, dk, dv, r, c, slots, scale_stride=S)
+    for n, p in enumerate(slots):
+        for h in range(H):
+            b = int(bits[h])
+            if b <= 8:
+                s = (r[p * S + h][:, None].astype(np.float64) * c[p * S + h][None, :]).astype(np.float32)
+                assert np.array_equal(L[n, h], (codes[n, h] * s.astype(np.float64)).astype(np.float32))
+            elif b == 16:
+                assert np.array_equal(L[n, h], X[n, h].astype(np.float16).astype(np.float32))
+            else:
+                assert np.array_equal(L[n, h], X[n, h])
+    q, k = _f32(_unit(rng, slots.size * H, dk)), _f32(_unit(rng, slots.size * H, dk))
+    v = _f32(rng.standard_normal((slots.size * H, dv)))
+    alpha = _f32(rng.uniform(0.5, 1, slots.size * H))
+    beta = _f32(rng.uniform(0, 1, slots.size * H))
+    ref = pool.copy()
+    o = orc.step_pool(pool, bits, dk, dv, r, c, slots, q, k, v, alpha, beta, scale_stride=S)
+    o2 = orc.readout_pool(pool, bits, dk, dv, r, c, slots, q, scale_stride=S)
+    for n, p in enumerate(slots):
+        for h in range(H):
+            b, lo, t = int(bits[h]), p * slab + off[h], n * H + h
+            tb = orc.tile_bytes(b, dk, dv)
+            tt, oo = orc.step_tile(b, dk, dv, ref[lo:lo + tb], r[p * S + h], c[p * S + h], q[t],
+                                   k[t], v[t], alpha[t], beta[t])
+            assert np.array_equal(pool[lo:lo + tb], tt)
+            assert np.array_equal(o[n, h], oo)
+            assert np.array_equal(o2[n, h], orc.readout_tile(b, dk, dv, tt, r[p * S + h],
+                                                              c[p * S + h], q[t]))
+
+
+def test_nonfinite_values_are_reported(orc):
+    """The step reports a tile when a value it stores from is not finite: for a
+    code, the fp32 quotient the code is decided on (so a finite update over a
+    vanishing step size counts); for an FP16/FP32 element, the value itself (a
+    finite value that overflows binary16 does not count).  A non-finite query
+    touches only the readout and is not reported."""
+    rng = np.random.default_rng(81)
+    dk, dv = 16, 16
+    tile, r, c, codes, s = _quant_tile(orc, rng, 8, dk, dv)
+    q, k = _f32(_unit(rng, 1, dk)[0]), _f32(_unit(rng, 1, dk)[0])
+    v = _f32(rng.standard_normal(dv))
+    t0, o0, bad = orc.step_tile(8, dk, dv, tile, r, c, q, k, v, 0.9, 0.5, return_flag=True)
+    assert not bad
+    _, _, bad = orc.step_tile(8, dk, dv, tile, r, c, q, k, v, np.nan, 0.5, return_flag=True)
+    assert bad
+    vb = v.copy()
+    vb[3] = np.inf
+    t, _, bad = orc.step_tile(8, dk, dv, tile, r, c, q, k, vb, 0.9, 0.5, return_flag=True)
+    assert bad
+    got = np.round(orc.decode_tile(8, dk, dv, t, r, c) / s)
+    # column 3 saturates by the sign of k_i (beta > 0); the other columns are unaffected
+    assert np.array_equal(got[:, 3], np.where(k > 0, 127, -127))
+    assert np.array_equal(np.delete(got, 3, 1),
+                          np.delete(np.round(orc.decode_tile(8, dk, dv, t0, r, c) / s), 3, 1))
+    qb = q.copy()
+    qb[0] = np.nan
+    t, o, bad = orc.step_tile(8, dk, dv, tile, r, c, qb, k, v, 0.9, 0.5, return_flag=True)
+    assert not bad and np.array_equal(t, t0) and np.all(np.isnan(o))
+    # a step size of 1e-40 (a binary32 subnormal): the update is finite, the quotient is not
+    rt, ct = np.full(dk, 1e-20, np.float32), np.full(dv, 1e-20, np.float32)
+    tt = orc.encode_tile(8, dk, dv, np.zeros((dk, dv)), rt, ct)
+    t, _, bad = orc.step_tile(8, dk, dv, tt, rt, ct, q, k, v, 0.9, 0.5, return_flag=True)
+    assert bad
+    x = 0.5 * k[:, None].astype(np.float64) * v[None, :]
+    got = np.array([[orc.field_get(t, 8, orc.elem_index(i, j, dv)) for j in range(dv)]
+                    for i in range(dk)]).astype(np.int64) - 128
+    assert np.array_equal(got, np.where(x > 0, 127, np.where(x < 0, -127, 0)))
+    # FP16 / FP32 elements: reported on the fp32 value; 1e5 overflows binary16 only
+    one_r, one_c = np.ones(dk, np.float32), np.ones(dv, np.float32)
+    big = np.zeros((dk, dv))
+    big[1, 2] = 1e5
+    t16, bad = orc.encode_tile(16, dk, dv, big, one_r, one_c, return_flag=True)
+    assert not bad and orc.field_get(t16, 16, orc.elem_index(1, 2, dv)) == 0x7C00
+    big[1, 2] = 1e39
+    _, bad = orc.encode_tile(32, dk, dv, big, one_r, one_c, return_flag=True)
+    assert bad
+    big[1, 2] = np.nan
+    _, bad = orc.encode_tile(16, dk, dv, big, one_r, one_c, return_flag=True)
+    assert bad
+
+
+def test_pool_counts_reported_tiles(orc):
+    rng = np.random.default_rng(82)
+    dk = dv = 16
+    bits = np.array([4, 8, 16, 32], np.uint8)
+    H = bits.size
+    off, slab = orc.pool_layout(bits, dk, dv)
+    r = _f32(rng.uniform(0.5, 2, (H, dk)))
+    c = _f32(rng.uniform(0.01, 0.05, (H, dv)))
+    S0 = _f32(rng.normal(0, 0.2, (3, H, dk, dv)))
+    pool = np.zeros(3 * slab, np.uint8)
+    slots = np.array([2, 0, 1], np.int32)
+    assert orc.store_pool(pool, bits, dk, dv, r, c, slots, S0) == 0
+    S1 = S0.copy()
+    S1[1, 2, 0, 0] = np.inf
+    S1[2, 0, 5, 5] = np.nan
+    assert orc.store_pool(pool.copy(), bits, dk, dv, r, c, slots, S1) == 2
+    n = slots.size
+    q, k = _f32(_unit(rng, n * H, dk)), _f32(_unit(rng, n * H, dk))
+    v = _f32(rng.standard_normal((n * H, dv)))
+    alpha, beta = _f32(rng.uniform(0.5, 1, n * H)), _f32(rng.uniform(0, 1, n * H))
+    _, bad = orc.step_pool(pool.copy(), bits, dk, dv, r, c, slots, q, k, v, alpha, beta,
+                           return_flagged=True)
+    assert bad == 0
+    alpha[1 * H + 3] = np.nan  # request 1, head 3
+    beta[2 * H + 0] = np.inf   # request 2, head 0
+    q[0, 0] = np.nan           # readout only
+    _, bad = orc.step_pool(pool.copy(), bits, dk, dv, r, c, slots, q, k, v, alpha, beta,
+                           return_flagged=True)
+    assert bad == 2
+    ab = _f32(rng.uniform(0.5, 1, (n * H, dk)))
+    _, bad = orc.step_pool_kda(pool.copy(), bits, dk, dv, r, c, slots, q, k, v, ab,
+                               _f32(rng.uniform(0, 1, n * H)), return_flagged=True)
+    assert bad == 0
+    ab[4, 7] = np.nan
+    _, bad = orc.step_pool_kda(pool.copy(), bits, dk, dv, r, c, slots, q, k, v, ab,
+                               _f32(rng.uniform(0, 1, n * H)), return_flagged=True)
+    assert bad == 1
