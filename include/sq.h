@@ -64,8 +64,17 @@
  *   - Non-finite inputs (alpha, beta, q, k, v, scales) are a caller error.  The
  *     result is defined on the updated value as the kernel evaluates it: a
  *     NaN quotient S'/s becomes code 0, +-Inf the nearest bound +-Q; FP16,
- *     BF16 and FP32 heads store the non-finite value.  Either way the pool's
- *     sticky flag is set (sq_pool_last_device_error).
+ *     BF16 and FP32 heads store the non-finite value.  The pages say nothing
+ *     of non-finite values; this rule is a reading.  A NaN or infinite gate,
+ *     write strength, key or value element gives the same stored result
+ *     in any evaluation order; an infinite gate does not (its codes are
+ *     then unspecified within [-Q, Q]).  A non-finite query only reaches the
+ *     readout o.  Whenever a stored value comes from a non-finite one, the
+ *     pool's sticky flag is set (sq_pool_last_device_error).  The d = 128
+ *     code-tile kernel takes that decision on the update's factors (the
+ *     gate, beta k_i / r_i, (v_j - alpha u_j) / c_j), the others on each
+ *     value; the two agree unless finite factors overflow fp32 in their
+ *     product, which takes step sizes near the bottom of the fp32 range.
  *   - d_k and d_v must be multiples of 4 and at most 256; d_k = d_v = 128 takes
  *     the tuned kernels, other shapes a plain one.
  */

@@ -934,8 +934,9 @@ __device__ __forceinline__ void tile128(const StepArgs &a, uint32_t n, uint32_t 
         if constexpr (CHG) sm.pa[tr] = make_float4(ai, gate * us, OFF * (1.0f - gate) - BIAS, 0.0f);
         else if (UPDATE) sm.a[tr] = ai;
         sm.vc[tr] = make_float2(vj, cjs);
-        // a non-finite row factor or gate sets the pool's sticky flag
-        if (__ballot(!__builtin_isfinite(fabsf(ai) + fabsf(CHG ? gate : alpha))) && (t & 63) == 0)
+        // a non-finite row factor or gate of a step sets the pool's sticky flag
+        if (UPDATE && __ballot(!__builtin_isfinite(fabsf(ai) + fabsf(CHG ? gate : alpha))) &&
+            (t & 63) == 0)
             a.err[0] = 1;
         const float s0 = wave_sum_row3(qi * ki), s1 = wave_sum_row3(wi), s2 = wave_sum_row3(gi);
         if (t < 128 && (t & 63) == 48)

@@ -5,7 +5,12 @@
  *   - alpha = 1, beta = 1, k = e_m: row m of the state becomes v (write into
  *     a row of the gated delta rule), other rows keep their values;
  *   - the readout o = S'^T q with q = e_m is v for the FP32 head;
- *   - sq_check_slots flags a repeated slot.
+ *   - sq_check_slots flags a repeated slot;
+ *   - with scale_slot_stride = H every slot has its own factors: a 4-bit
+ *     state stored with step 1/4 in slot 1 and 1/8 in slot 0 loads back as
+ *     rne(x / step) * step of its own slot;
+ *   - a NaN stored sets the pool's sticky flag (code 0 is stored), which
+ *     sq_pool_last_device_error reads and clears.
  * Exit status 0 on success; prints the failing check otherwise.
  */
 #include <hip/hip_runtime_api.h>
@@ -129,7 +134,63 @@ int main(void)
 
     CHECK(sq_decode_step(pool, (const int32_t *)ids, SLOTS, q, k, v, 7, (const float *)alpha,
                          (const float *)beta, NULL, NULL) == SQ_ERR_INVALID, "bad dtype rejected");
+    CHECK(sq_pool_last_device_error(pool, NULL) == SQ_OK, "no non-finite value met");
     sq_pool_free(pool);
+
+    /* per-slot factors: vector p * H + h holds the factors of slot p, head h */
+    float *h_r2 = malloc(sizeof(float) * SLOTS * H * D), *h_c2 = malloc(sizeof(float) * SLOTS * H * D);
+    for (int p = 0; p < SLOTS; p++)
+        for (int i = 0; i < H * D; i++) {
+            h_r2[p * H * D + i] = 1.0f;
+            h_c2[p * H * D + i] = p == 1 ? 0.25f : 0.125f;
+        }
+    void *r2, *c2, *state2, *ids2;
+    CHECK(hipMalloc(&r2, sizeof(float) * SLOTS * H * D) == hipSuccess, "hipMalloc r2");
+    CHECK(hipMalloc(&c2, sizeof(float) * SLOTS * H * D) == hipSuccess, "hipMalloc c2");
+    CHECK(hipMalloc(&state2, nbytes) == hipSuccess, "hipMalloc state2");
+    CHECK(hipMalloc(&ids2, sizeof(int32_t) * SLOTS) == hipSuccess, "hipMalloc ids2");
+    hipMemcpy(r2, h_r2, sizeof(float) * SLOTS * H * D, hipMemcpyHostToDevice);
+    hipMemcpy(c2, h_c2, sizeof(float) * SLOTS * H * D, hipMemcpyHostToDevice);
+    const int32_t h_ids2[SLOTS] = {0, 1};
+    hipMemcpy(ids2, h_ids2, sizeof(h_ids2), hipMemcpyHostToDevice);
+    desc.row_scale = (const float *)r2;
+    desc.col_scale = (const float *)c2;
+    desc.scale_slot_stride = H;
+    desc.state = state2;
+    sq_pool *pool2 = NULL;
+    CHECK(sq_pool_alloc(&desc, &pool2) == SQ_OK && pool2, "sq_pool_alloc with a slot stride");
+    desc.scale_slot_stride = H - 1;
+    sq_pool *bad = NULL;
+    CHECK(sq_pool_alloc(&desc, &bad) == SQ_ERR_INVALID && !bad, "slot stride below n_heads rejected");
+    CHECK(sq_pool_store(pool2, (const int32_t *)ids2, SLOTS, (const float *)S, NULL) == SQ_OK, "store 2");
+    CHECK(sq_pool_load(pool2, (const int32_t *)ids2, SLOTS, (float *)out, NULL) == SQ_OK, "load 2");
+    CHECK(hipDeviceSynchronize() == hipSuccess, "synchronize 2");
+    hipMemcpy(h_out, out, sizeof(float) * SLOTS * H * D * D, hipMemcpyDeviceToHost);
+    for (int n = 0; n < SLOTS; n++)
+        for (int h = 0; h < H; h++)
+            for (long e = 0; e < (long)D * D; e++) {
+                const float x = h_S[((long)n * H + h) * D * D + e];
+                const float step = n == 1 ? 0.25f : 0.125f;
+                const float want = h == 0 ? nearbyintf(x / step) * step : x; /* |x / step| <= 7 */
+                if (h_out[((long)n * H + h) * D * D + e] != want) {
+                    fprintf(stderr, "abi_smoke: slot %d head %d element %ld: %g, want %g\n", n, h, e,
+                            h_out[((long)n * H + h) * D * D + e], want);
+                    return 1;
+                }
+            }
+    CHECK(sq_pool_last_device_error(pool2, NULL) == SQ_OK, "finite store leaves the flag clear");
+
+    /* a NaN stored: code 0, and the flag is set until read */
+    h_S[5] = NAN;
+    hipMemcpy(S, h_S, sizeof(float) * D * D, hipMemcpyHostToDevice);
+    CHECK(sq_pool_store(pool2, (const int32_t *)ids2, 1, (const float *)S, NULL) == SQ_OK, "store NaN");
+    CHECK(sq_pool_last_device_error(pool2, NULL) == SQ_ERR_DEVICE, "NaN sets the flag");
+    CHECK(sq_pool_last_device_error(pool2, NULL) == SQ_OK, "the flag is cleared once read");
+    CHECK(sq_pool_load(pool2, (const int32_t *)ids2, 1, (float *)out, NULL) == SQ_OK, "load 3");
+    CHECK(hipDeviceSynchronize() == hipSuccess, "synchronize 3");
+    hipMemcpy(h_out, out, sizeof(float) * D * D, hipMemcpyDeviceToHost);
+    CHECK(h_out[5] == 0.0f && h_out[4] == h_S[4], "a NaN stores code 0");
+    sq_pool_free(pool2);
     printf("abi_smoke ok\n");
     return 0;
 }

@@ -64,6 +64,7 @@ def _desc(sq, **kw):
     (dict(n_slots=0), -1), (dict(n_heads=0), -1), (dict(state=None), -1), (dict(state=0x100010), -1),
     (dict(row_scale=None), -1), (dict(col_scale=0x20004), -1), (dict(state_bytes=100), -1),
     (dict(bits=[8, 3]), -2), (dict(d_k=18), -2), (dict(d_v=260), -2),
+    (dict(scale_slot_stride=1), -1), (dict(scale_slot_stride=-2), -1),
 ])
 def test_pool_alloc_validates_before_any_hip_call(sq, kw, status):
     desc, keep = _desc(sq, **kw)
@@ -176,3 +177,6 @@ def test_binding_checks_pool_alloc_scales(sq, monkeypatch):
         sq.sq_pool_alloc(2, 2, 16, 16, [8, 4], r, r[0], state)
     with pytest.raises(sq.SqError, match="row_scale is not on a GPU"):
         sq.sq_pool_alloc(2, 2, 16, 16, [8, 4], torch.ones(2, 16), r, state)
+    # with a slot stride S the factor arrays hold n_slots * S vectors
+    with pytest.raises(sq.SqError, match="row_scale has 32 elements, expected 96"):
+        sq.sq_pool_alloc(2, 2, 16, 16, [8, 4], r, r, state, scale_slot_stride=3)

@@ -3,16 +3,20 @@ times (one sq_decode_step over the whole batch).
 
 The pools are initialised on the GPU with sq_pool_store; sampled tiles of the
 store are checked bit-exact against the oracle's encoding of the same fp32
-states.  On checked steps, sampled tiles (every head of one request plus a
-random set covering every width) are copied back before and after the step
-and the oracle steps them, teacher-forced, with the same inputs."""
+states.  Every step is checked, teacher-forced: on the first two and the last
+step the whole pool is copied back before and after the step and the oracle
+steps every tile; on the other steps a fixed sample (every head of two
+requests, 4,096 random tiles and a few of every width) is copied back and
+stepped tile by tile."""
 import concurrent.futures as cf
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_harness import Tally, host_f32, say
+import time
+
+from gpu_harness import Tally, compare_pools_fast, host_f32, say
 from quantized_recurrent_state_gated_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -41,16 +45,21 @@ class DevicePool:
         self.rh, self.ch = self.r.cpu().numpy(), self.c.cpu().numpy()
 
     def tile_bytes(self, tiles):
-        """uint8 copies of tiles [(n, h)] (slot n holds request n)."""
-        out = []
+        """uint8 copies of tiles [(n, h)] (slot n holds request n), gathered on
+        the GPU and copied back in one transfer."""
+        views, sizes = [], []
         for n, h in tiles:
             off, nb = self.sq.sq_pool_tile_offset(self.pool, int(n), int(h))
-            out.append(self.state[off:off + nb])
-        return [t.cpu().numpy() for t in out]
+            views.append(self.state[off:off + nb])
+            sizes.append(nb)
+        flat = torch.cat(views).cpu().numpy()
+        return np.split(flat, np.cumsum(sizes)[:-1])
 
 
 def sample(w, bits, rng, n_random):
-    tiles = [(int(rng.integers(w.n_req)), h) for h in range(w.n_heads)]
+    """Every head of two requests, n_random random tiles, 8 of every width."""
+    reqs = rng.choice(w.n_req, size=min(2, w.n_req), replace=False)
+    tiles = [(int(n), h) for n in reqs for h in range(w.n_heads)]
     tiles += [(int(rng.integers(w.n_req)), int(rng.integers(w.n_heads))) for _ in range(n_random)]
     for b in sorted(set(int(x) for x in bits)):  # every width, several requests
         hs = np.nonzero(bits == b)[0]
@@ -92,59 +101,96 @@ def check_step(orc, dp, tiles, si, pre, post, o, tally, kda=False):
     tally.add_o(np.stack([o_gpu[n, h] for n, h in tiles]), np.stack([r[1] for r in res]))
 
 
-def run_fullsize(sq, orc, name, check_steps, n_random=2048, all_tiles_at=(), kda=False):
-    """kda: step with sq_decode_step_kda and per-channel gates I.channel_gates."""
+def check_full(orc, dp, si, pre, post, o, tally, kda=False):
+    """Every tile of the pool: the oracle steps the whole pre-step image."""
+    w = dp.w
+    ref = pre.copy()
+    step = orc.step_pool_kda if kda else orc.step_pool
+    o_ref = step(ref, dp.bits, w.dk, w.dv, dp.rh, dp.ch, np.arange(w.n_req, dtype=np.int32),
+                 host_f32(si.q), host_f32(si.k), host_f32(si.v), host_f32(si.alpha),
+                 host_f32(si.beta), n_threads=THREADS)
+    off, slab = orc.pool_layout(dp.bits, w.dk, w.dv)
+    compare_pools_fast(tally, post, ref, dp.bits, off, slab, range(w.n_req), w.dk, w.dv)
+    tally.add_o(o.cpu().numpy(), o_ref)
+
+
+def run_fullsize(sq, orc, name, last, n_random=4096, full_at=None, kda=False, sample_every=1):
+    """Steps 0..last; every tile checked on full_at (default: 0, 1, last), the
+    fixed sample on every sample_every-th other step.  kda: step with
+    sq_decode_step_kda and per-channel gates I.channel_gates."""
     w = I.WORKLOADS[name]
-    say(f"[{name}{' kda' if kda else ''}] init {w.n_req} x {w.n_heads}")
+    full_at = (0, 1, last) if full_at is None else full_at
+    label = f"{name}{' kda' if kda else ''}"
+    t_start = time.time()
+    say(f"[{label}] init {w.n_req} x {w.n_heads}")
     dp = DevicePool(sq, w)
     rng = np.random.default_rng(7)
     tiles = sample(w, dp.bits, rng, n_random)
     check_store(orc, dp, tiles)
-    say(f"[{name}] store bit-exact on {len(tiles)} sampled tiles")
+    say(f"[{label}] store bit-exact on {len(tiles)} sampled tiles")
     o = torch.empty(w.n_req, w.n_heads, w.dv, device="cuda")
     tally = Tally()
-    every = [(n, h) for n in range(w.n_req) for h in range(w.n_heads)]
-    for t in range(max(check_steps) + 1):
+    full_tiles = 0
+    for t in range(last + 1):
         si = I.step_inputs(w, t, "cuda")
         if kda:
             si.alpha = I.channel_gates(w, t, "cuda")
-        check = t in check_steps
-        sel = every if t in all_tiles_at else tiles
-        if check:
-            pre = dp.tile_bytes(sel)
+        full = t in full_at
+        sampled = not full and t % sample_every == 0
+        if full:
+            torch.cuda.synchronize()
+            pre = dp.state.cpu().numpy()
+        elif sampled:
+            pre = dp.tile_bytes(tiles)
         step = sq.sq_decode_step_kda if kda else sq.sq_decode_step
         step(dp.pool, dp.slots, si.q, si.k, si.v, si.alpha, si.beta, o)
-        if check:
-            torch.cuda.synchronize()
-            post = dp.tile_bytes(sel)
-            check_step(orc, dp, sel, si, pre, post, o, tally, kda)
-            say(f"[{name}] step {t} ({len(sel)} tiles): {tally.summary()}")
+        torch.cuda.synchronize()
+        if full:
+            post = dp.state.cpu().numpy()
+            check_full(orc, dp, si, pre, post, o, tally, kda)
+            full_tiles += w.n_req * w.n_heads
+            del pre, post
+        elif sampled:
+            check_step(orc, dp, tiles, si, pre, dp.tile_bytes(tiles), o, tally, kda)
+        if full or t % (8 * sample_every) == 0:
+            say(f"[{label}] {time.time() - t_start:.0f}s step {t} "
+                f"({'every tile' if full else f'{len(tiles)} tiles'}): {tally.summary()}")
     tally.check()
+    assert full_tiles == len(full_at) * w.n_req * w.n_heads
+    assert sq.sq_pool_last_device_error(dp.pool) == sq.SQ_OK
 
 
+@pytest.mark.timeout(900)
 def test_serving_full_size(sq, orc):
-    run_fullsize(sq, orc, "serving", check_steps=(0, 1, 63))
+    """70 x 2304 heads, 64 steps: 161,280 tiles on steps 0, 1 and 63."""
+    run_fullsize(sq, orc, "serving", last=63)
 
 
+@pytest.mark.timeout(900)
 def test_highconc_full_size(sq, orc):
-    run_fullsize(sq, orc, "highconc", check_steps=(0, 1, 31))
+    """256 x 2304 heads (88 % 4-bit), 32 steps: 589,824 tiles on steps 0, 1 and 31."""
+    run_fullsize(sq, orc, "highconc", last=31)
 
 
+@pytest.mark.timeout(900)
 def test_drift_full_length(sq, orc):
-    """2048 steps; every tile checked at steps 0, 1, 1024, 2047, a sample of
-    tiles every 128 steps."""
-    steps = tuple(range(0, 2048, 128)) + (1, 1024, 2047)
-    run_fullsize(sq, orc, "drift", check_steps=steps, n_random=256, all_tiles_at=(0, 1, 1024, 2047))
+    """16 x 576 heads, 2048 steps: every tile on steps 0, 1, 1024 and 2047, a
+    sample of 256 tiles (plus two requests) every 16 steps."""
+    run_fullsize(sq, orc, "drift", last=2047, n_random=256, full_at=(0, 1, 1024, 2047),
+                 sample_every=16)
 
 
+@pytest.mark.timeout(900)
 def test_serving_full_size_channel_gate(sq, orc):
     """The per-key-channel-gate step at the serving size, in the launch bench.py times."""
-    run_fullsize(sq, orc, "serving", check_steps=(0, 1, 31), kda=True)
+    run_fullsize(sq, orc, "serving", last=31, kda=True)
 
 
+@pytest.mark.timeout(900)
 def test_highconc_full_size_channel_gate(sq, orc):
-    """The per-key-channel-gate step at 256 x 2304 heads (88 % 4-bit)."""
-    run_fullsize(sq, orc, "highconc", check_steps=(0, 1, 15), kda=True)
+    """The per-key-channel-gate step at 256 x 2304 heads (88 % 4-bit), 8 steps:
+    the sample on steps 0-6, every tile on step 7."""
+    run_fullsize(sq, orc, "highconc", last=7, kda=True, full_at=(7,))
 
 
 def test_serving_readout_full_size(sq, orc):
