@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -77,48 +78,77 @@ def traffic_from_profile(sha: str, workload: str, which: str = "step"):
 
 COPY_BYTES = 1 << 30  # the calibration copy of --copy-calibration
 
+# gfx950 L2-to-memory request counters, by request size (rocprofv3 -L):
+# reads of 32, 64 and 128 bytes, all reads; writes of 64 bytes, all writes
+# (a write is 32 or 64 bytes); TCC_BUBBLE counts 128-byte reads as well.
+READ_COUNTERS = ("TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B", "TCC_EA0_RDREQ")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_64B", "TCC_EA0_WRREQ", "TCC_BUBBLE")
+PMC_KERNELS = {"step": STEP_KERNEL, "channel_gate_step": KDA_KERNEL,
+               "copy": "copyBuffer"}  # the runtime's blit kernel of the 1 GiB copy
 
-def _pmc_rows(path, counter):
+
+def _pmc_dispatches(path, counters):
+    """{kernel key: [{counter: value} per dispatch, in dispatch order]} from a
+    rocprofv3 --pmc csv; dispatches missing a counter are dropped."""
     import csv
-    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-    step = [float(r["Counter_Value"]) * 1024 for r in rows if STEP_KERNEL in r["Kernel_Name"]]
-    kda = [float(r["Counter_Value"]) * 1024 for r in rows if KDA_KERNEL in r["Kernel_Name"]]
-    # the calibration copy is the runtime's blit kernel; torch's own copy and
-    # conversion kernels (other sizes) must not be taken for it
-    copies = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]]
-    return step, kda, copies
+    by = {k: {} for k in PMC_KERNELS}
+    for r in csv.DictReader(open(path)):
+        c = r["Counter_Name"]
+        if c not in counters:
+            continue
+        for key, name in PMC_KERNELS.items():
+            if name in r["Kernel_Name"]:
+                by[key].setdefault(int(r["Dispatch_Id"]), {})[c] = float(r["Counter_Value"])
+    return {k: [d[i] for i in sorted(d) if len(d[i]) == len(counters)] for k, d in by.items() if d}
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> int:
-    """HBM bytes per step launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    each scaled by the factor that makes the same counter read the known size
-    of the 1 GiB calibration copy."""
+def pmc_summary(read_csv: str, write_csv: str, workload: str) -> int:
+    """HBM bytes per launch from gfx950's per-request-size counters: reads =
+    32 n32 + 64 n64 + 128 n128, writes = 64 n64 + 32 (n - n64), per dispatch;
+    the median over the step's dispatches.  No scale factor: the 1 GiB
+    calibration copy (the largest blit dispatch) is reported beside as a check."""
     import statistics
-    fs, fk, fc = _pmc_rows(fetch_csv, "FETCH_SIZE")
-    ws, wk, wc = _pmc_rows(write_csv, "WRITE_SIZE")
-    ff = COPY_BYTES / max(fc)
-    fw = COPY_BYTES / max(wc)
+    rd = _pmc_dispatches(read_csv, READ_COUNTERS)
+    wr = _pmc_dispatches(write_csv, WRITE_COUNTERS)
 
-    def one(kernel, f, w):
-        fetch = statistics.median(f) * ff
-        write = statistics.median(w) * fw
-        return {"kernel": kernel, "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
-                "hbm_bytes_per_launch": fetch + write, "dispatches": [len(f), len(w)],
-                "raw_fetch_kib": statistics.median(f) / 1024,
-                "raw_write_kib": statistics.median(w) / 1024}
+    def rbytes(d):
+        return 32 * d[READ_COUNTERS[0]] + 64 * d[READ_COUNTERS[1]] + 128 * d[READ_COUNTERS[2]]
+
+    def wbytes(d):
+        return 64 * d[WRITE_COUNTERS[0]] + 32 * (d[WRITE_COUNTERS[1]] - d[WRITE_COUNTERS[0]])
+
+    def one(key):
+        r, w = rd[key], wr[key]
+        if key == "copy":
+            r, w = [max(r, key=rbytes)], [max(w, key=wbytes)]
+        read = statistics.median(rbytes(d) for d in r)
+        write = statistics.median(wbytes(d) for d in w)
+        return {"kernel": PMC_KERNELS[key], "fetch_bytes_per_launch": read,
+                "write_bytes_per_launch": write, "hbm_bytes_per_launch": read + write,
+                "dispatches": [len(r), len(w)],
+                "raw_median": {c: statistics.median(d[c] for d in r) for c in READ_COUNTERS} |
+                              {c: statistics.median(d[c] for d in w) for c in WRITE_COUNTERS},
+                # every dispatch: the sized read counts add up to all reads, and
+                # every write is a 64-byte one or the rest (32-byte)
+                "reads_by_size_sum_to_all": all(
+                    d[READ_COUNTERS[0]] + d[READ_COUNTERS[1]] + d[READ_COUNTERS[2]] ==
+                    d[READ_COUNTERS[3]] for d in r),
+                "tcc_bubble_reads": statistics.median(d[WRITE_COUNTERS[2]] for d in w)}
 
     wl = "" if workload == "serving" else f" --workload {workload}"
+    cmd = ("python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp32-baseline "
+           f"--no-copy-ceiling --copy-calibration{wl}")
     out = {"kernel_source_sha": kernel_source_sha(), "workload": workload,
-           "step": one(STEP_KERNEL, fs, ws),
-           "fetch_factor": ff, "write_factor": fw,
-           "calibration": "1 GiB device copy (hipMemcpy D2D blit kernel): FETCH_SIZE and WRITE_SIZE "
-                          "each scaled so that it reads 1 GiB",
-           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o <name> -- python3 "
-                        f"bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp32-baseline "
-                        f"--no-copy-ceiling --copy-calibration{wl}"
-                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
-    if fk and wk:
-        out["channel_gate_step"] = one(KDA_KERNEL, fk, wk)
+           "method": "per-request-size L2-to-memory counters, bytes per dispatch, no scale factor",
+           "commands": [f"rocprofv3 --pmc {' '.join(READ_COUNTERS)} --output-format csv "
+                        f"-d <dir> -o <name> -- {cmd}",
+                        f"rocprofv3 --pmc {' '.join(WRITE_COUNTERS)} --output-format csv "
+                        f"-d <dir> -o <name> -- {cmd}"]}
+    for key in ("step", "channel_gate_step", "copy"):
+        if key in rd and key in wr:
+            out[key] = one(key)
+    if "copy" in out:
+        out["copy"]["expected_bytes_each_way"] = COPY_BYTES
     path = traffic_file(workload)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
@@ -324,6 +354,14 @@ def copy_ceiling(dev, stream, nbytes=2 << 30, reps=10):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=30).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -334,41 +372,86 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, bits, get_pool, r, c, si, n_threads, target_s):
-    """The oracle, as it stands, on a bounded sample: whole requests (all 2304
-    heads) of the same workload, calibrated to about target_s seconds on
-    n_threads threads; then one thread on 1/n_threads of that sample."""
+def cpu_threads(requested=None):
+    """(threads, reason): the requested count; else the job's CPU share as the
+    environment states it (OMP_NUM_THREADS); else every core in the affinity mask."""
+    aff = len(os.sched_getaffinity(0))
+    if requested:
+        return int(requested), f"--cpu-threads {requested} ({aff} cores in the affinity mask)"
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env), (f"OMP_NUM_THREADS={env}: the job's CPU share ({aff} cores in the "
+                          f"affinity mask, shared with other jobs)")
+    return aff, f"every core in the affinity mask ({aff})"
+
+
+def oracle_steps(w, bits, pool, r, c, inputs, n_req, threads):
+    """Wall time of the oracle stepping requests 0..n_req-1 of a host pool once
+    per input in `inputs` (in place)."""
     import numpy as np
     import oracle
 
-    q = si.q.float().cpu().numpy()
-    k = si.k.float().cpu().numpy()
-    v = si.v.float().cpu().numpy()
-    al = si.alpha.cpu().numpy()
-    be = si.beta.cpu().numpy()
-
-    def run(n, threads):
-        slots = np.arange(n, dtype=np.int32)
-        pool = get_pool(n)
+    slots = np.arange(n_req, dtype=np.int32)
+    total = 0.0
+    for si in inputs:
+        q, k, v = (x[:n_req].float().cpu().numpy() for x in (si.q, si.k, si.v))
+        al, be = si.alpha[:n_req].cpu().numpy(), si.beta[:n_req].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.step_pool(pool, bits, w.dk, w.dv, r, c, slots, q[:n], k[:n], v[:n], al[:n], be[:n],
-                         n_threads=threads)
-        return time.perf_counter() - t0
+        oracle.step_pool(pool, bits, w.dk, w.dv, r, c, slots, q, k, v, al, be, n_threads=threads,
+                         want_o=True)
+        total += time.perf_counter() - t0
+    return total
 
-    t1 = run(1, n_threads)
-    n = max(1, min(w.n_req, int(target_s / max(t1, 1e-3))))
-    tn = run(n, n_threads) if n > 1 else t1
-    out = {"value": n * w.n_heads / tn, "unit": "heads*tokens/s", "cores": n_threads,
-           "kind": "oracle", "cpu": cpu_model(),
-           "sample": f"{n} of {w.n_req} requests x all {w.n_heads} heads, one decode step "
-                     f"({n * w.n_heads} tiles, {tn:.1f} s wall on {n_threads} threads)"}
+
+def cpu_baseline(w, bits, host_pool, r, c, inputs, n_threads, why, other=None):
+    """The oracle, as it stands: len(inputs) full decode steps of workload w on
+    n_threads threads (every tile of every request), then one thread on
+    1/n_threads of the requests for one step.  other = (workload, bits, host
+    pool, r, c, inputs): one full step of a second workload on n_threads."""
+    pool = host_pool.copy()
+    t = oracle_steps(w, bits, pool, r, c, inputs, w.n_req, n_threads)
+    n_steps = len(inputs)
+    out = {"value": n_steps * w.n_req * w.n_heads / t, "unit": "heads*tokens/s",
+           "cores": n_threads, "cores_why": why, "kind": "oracle", "cpu": cpu_model(),
+           "sample": f"{n_steps} full decode steps of {w.name} ({w.n_req} requests x {w.n_heads} "
+                     f"heads = {w.n_req * w.n_heads} tiles per step), {t:.1f} s wall on "
+                     f"{n_threads} threads",
+           "s_per_step": t / n_steps}
     if n_threads > 1:
-        n1 = max(1, n // n_threads)
-        t = run(n1, 1)
-        out["one_core"] = {"value": n1 * w.n_heads / t, "unit": "heads*tokens/s",
-                           "sample": f"{n1} of {w.n_req} requests x all {w.n_heads} heads "
-                                     f"({n1 * w.n_heads} tiles, {t:.1f} s on 1 thread)"}
+        n1 = max(1, w.n_req // n_threads)
+        pool = host_pool.copy()
+        t1 = oracle_steps(w, bits, pool, r, c, inputs[:1], n1, 1)
+        out["one_core"] = {"value": n1 * w.n_heads / t1, "unit": "heads*tokens/s",
+                           "sample": f"{n1} of {w.n_req} requests x all {w.n_heads} heads, one "
+                                     f"step ({n1 * w.n_heads} tiles, {t1:.1f} s on 1 thread)"}
+    if other is not None:
+        w2, bits2, pool2, r2, c2, in2 = other
+        t2 = oracle_steps(w2, bits2, pool2, r2, c2, in2, w2.n_req, n_threads)
+        out[w2.name] = {"value": len(in2) * w2.n_req * w2.n_heads / t2, "unit": "heads*tokens/s",
+                        "s_per_step": t2 / len(in2),
+                        "sample": f"{len(in2)} full decode step(s) of {w2.name} ({w2.n_req} x "
+                                  f"{w2.n_heads} = {w2.n_req * w2.n_heads} tiles), {t2:.1f} s "
+                                  f"wall on {n_threads} threads"}
     return out
+
+
+def host_pool_of(sq, I, name, dev):
+    """A workload's pool, initialised on the GPU from its seeded initial
+    states, copied to host memory; returns (workload, bits, pool, r, c)."""
+    import torch
+
+    w = I.WORKLOADS[name]
+    bits = I.head_bits(w)
+    r, c = I.scales(w, device=dev)
+    nbytes = sq.sq_pool_bytes(w.n_req, w.n_heads, w.dk, w.dv, bits)
+    state = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pool = sq.sq_pool_alloc(w.n_req, w.n_heads, w.dk, w.dv, bits, r, c, state)
+    slots = torch.arange(w.n_req, dtype=torch.int32, device=dev)
+    for p in range(w.n_req):
+        sq.sq_pool_store(pool, slots[p:p + 1], I.initial_state(w, p, dev))
+    host = state.cpu().numpy()
+    sq.sq_pool_free(pool)
+    return w, bits, host, r.cpu().numpy(), c.cpu().numpy()
 
 
 def main() -> int:
@@ -382,8 +465,12 @@ def main() -> int:
     ap.add_argument("--workload", default="serving", choices=["serving", "highconc", "layer", "drift"])
     ap.add_argument("--distinct-inputs", type=int, default=16,
                     help="distinct pre-generated step inputs, cycled over the timed steps")
-    ap.add_argument("--cpu-threads", type=int, default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="oracle threads (default: OMP_NUM_THREADS, else every core in the affinity mask)")
+    ap.add_argument("--cpu-steps", type=int, default=2,
+                    help="full decode steps of the workload the CPU oracle times")
+    ap.add_argument("--cpu-other", default="highconc",
+                    help="a second workload the CPU oracle times one full step of ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-baseline", action="store_true",
                     help="skip timing the unquantized FP32- and BF16-state steps at the same shape")
@@ -396,9 +483,10 @@ def main() -> int:
                     help="skip timing the per-key-channel-gate step at the same shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "`bench.py --copy-calibration` into profiles/ and exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("READ_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of `bench.py --copy-calibration` "
+                         "(the read-request and the write-request counters, by size) into "
+                         "profiles/ and exit")
     ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
                     help="print the step kernel's row of a rocprofv3 --stats csv and exit")
     args = ap.parse_args()
@@ -559,16 +647,18 @@ def main() -> int:
         del ins
         torch.cuda.synchronize()
         log("[bench] CPU oracle baseline ...")
-        n_cpu = args.cpu_threads or min(len(os.sched_getaffinity(0)), 16)
-        si = I.step_inputs(w, 0, dev)
-        slab = nbytes // w.n_req
-
-        def get_pool(n):
-            return state[: n * slab].cpu().numpy()
-
-        result["cpu_baseline"] = cpu_baseline(w, bits, get_pool, r.cpu().numpy(), c.cpu().numpy(),
-                                              si, n_cpu, args.cpu_seconds)
-        log(f"[bench] CPU oracle: {result['cpu_baseline']['value']:.3e} heads*tokens/s")
+        n_cpu, why = cpu_threads(args.cpu_threads)
+        host = state.cpu().numpy()
+        other = None
+        if args.cpu_other and args.cpu_other != w.name:
+            w2, bits2, pool2, r2, c2 = host_pool_of(sq, I, args.cpu_other, dev)
+            other = (w2, bits2, pool2, r2, c2, [I.step_inputs(w2, 0)])
+            torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(
+            w, bits, host, r.cpu().numpy(), c.cpu().numpy(),
+            [I.step_inputs(w, t) for t in range(args.cpu_steps)], n_cpu, why, other)
+        log(f"[bench] CPU oracle: {result['cpu_baseline']['value']:.3e} heads*tokens/s "
+            f"on {n_cpu} threads")
     print(json.dumps(result), flush=True)
     return 0
 
