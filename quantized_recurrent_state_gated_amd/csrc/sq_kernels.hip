@@ -354,6 +354,33 @@ __host__ __forceinline__ uint32_t xcd_grid(uint32_t n_req, uint32_t H)
     return (n_req * H + kXcds - 1) / kXcds * kXcds;
 }
 
+// Two tiles per workgroup: workgroup g holds the tiles that workgroups
+// 2 (g / 8) * 8 + g % 8 and that + 8 would hold alone, i.e. tiles 2i and
+// 2i + 1 of XCD g % 8's walk (half = 0, 1).
+__device__ __forceinline__ bool xcd_tile_pair(uint32_t n_req, uint32_t H, const uint32_t (&xm)[8],
+                                              uint32_t half, uint32_t &n, uint32_t &h)
+{
+    const uint32_t x = blockIdx.x % kXcds, i = 2 * (blockIdx.x / kXcds) + half;
+    if (H >= kXcdGroupMin) {
+        const uint32_t h0 = (uint32_t)((uint64_t)x * H / kXcds);
+        const uint32_t hx = (uint32_t)((uint64_t)(x + 1) * H / kXcds) - h0;
+        n = div_magic(i, hx, xm[x]);
+        h = h0 + (i - n * hx);
+        return n < n_req;
+    }
+    const uint32_t total = n_req * H, per = (total + kXcds - 1) / kXcds, b = x * per + i;
+    n = div_magic(b, H, xm[0]);
+    h = b - n * H;
+    return i < per && b < total;
+}
+
+__host__ __forceinline__ uint32_t xcd_grid_pair(uint32_t n_req, uint32_t H)
+{
+    const uint32_t per = H >= kXcdGroupMin ? n_req * ((H + kXcds - 1) / kXcds)
+                                           : (n_req * H + kXcds - 1) / kXcds;
+    return (per + 1) / 2 * kXcds;
+}
+
 static uint32_t magic_of(uint32_t d) { return d <= 1 ? 0u : (uint32_t)(((1ull << 32) + d - 1) / d); }
 
 // the reciprocals xcd_tile needs for H heads
@@ -891,7 +918,9 @@ __device__ __forceinline__ void tile128(const StepArgs &a, uint32_t n, uint32_t 
     constexpr uint32_t MSTEP = RG * 32 * BLK;  // bytes between a thread's blocks
     constexpr bool NT = QUANT;                 // code tiles stream nontemporally (measured faster)
 
-    const int t = threadIdx.x;
+    // the tile's own thread index (a 256-thread workgroup may hold two
+    // 128-thread tiles, one per half)
+    const int t = threadIdx.x & (TPB - 1);
     const int cb = t & 31, rg = t >> 5, tr = t & 127;
     const size_t nh = (size_t)n * (uint32_t)a.H + h;
     const int32_t slot = sload(a.slot_ids + n);
@@ -1092,6 +1121,28 @@ __global__ __launch_bounds__(TPB) __attribute__((amdgpu_waves_per_eu(WPE, 8))) v
     case 8: tile128<8, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
     case 6: tile128<6, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
     case 4: tile128<4, T, UPDATE, CHG, TPB>(f.a, n, h, sm); break;
+    default: break;
+    }
+}
+
+// The same step with two 128-thread tiles per 256-thread workgroup (each half
+// runs tile128 on its own tile and shared memory; the halves meet at every
+// barrier, and a half with no tile, or an FP32/BF16 head, simply ends).
+// Measured on full serving launches: a memory-only copy of the step moves its
+// bytes 5-6 % faster with two tiles per workgroup than with one.
+template <typename T, bool UPDATE, bool CHG, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void k_step128x2(FusedArgs f)
+{
+    using SM = typename std::conditional<CHG, SmemFusedK, SmemFused>::type;
+    __shared__ SM sm[2];
+    const uint32_t half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);  // uniform per wave
+    uint32_t n, h;
+    if (!xcd_tile_pair((uint32_t)f.a.n_req, (uint32_t)f.a.H, f.a.xm, half, n, h)) return;
+    switch (sload(f.head_bits + h)) {
+    case 16: tile128<16, T, UPDATE, CHG, 128>(f.a, n, h, sm[half]); break;
+    case 8: tile128<8, T, UPDATE, CHG, 128>(f.a, n, h, sm[half]); break;
+    case 6: tile128<6, T, UPDATE, CHG, 128>(f.a, n, h, sm[half]); break;
+    case 4: tile128<4, T, UPDATE, CHG, 128>(f.a, n, h, sm[half]); break;
     default: break;
     }
 }
@@ -1413,7 +1464,19 @@ static void fused128(Op op, bool qkv_bf16, const FusedArgs &f, dim3 grid, hipStr
     else fused128_t<float, TPB, WPE>(op, f, grid, st);
 }
 
-// tile counts that take the 256-thread launch
+template <typename T>
+static void fused128x2_t(Op op, const FusedArgs &f, dim3 grid, hipStream_t st)
+{
+    if (op == OP_STEP)
+        hipLaunchKernelGGL((k_step128x2<T, true, false, 5>), grid, dim3(256), 0, st, f);
+    else if (op == OP_STEP_KDA)
+        hipLaunchKernelGGL((k_step128x2<T, true, true, 5>), grid, dim3(256), 0, st, f);
+    else
+        hipLaunchKernelGGL((k_step128x2<T, false, false, 5>), grid, dim3(256), 0, st, f);
+}
+
+// tile counts that take the 256-thread launch (four waves per tile); larger
+// launches pair two 128-thread tiles per workgroup
 constexpr uint32_t kWideTilesMin = 1024, kWideTilesMax = 16384;
 
 hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_blocks,
@@ -1431,10 +1494,15 @@ hipError_t launch_fused128(Op op, bool qkv_bf16, const FusedArgs &f, uint32_t n_
     // blocks per thread, 8 waves per SIMD) finish each tile sooner.
     // Measured: 3,360-13,440 tiles 4-7 % faster with 256 threads, 20,160 equal,
     // 40,320 and more 4-5 % slower.
-    if (n_blocks >= kWideTilesMin && n_blocks < kWideTilesMax)
+    if (n_blocks >= kWideTilesMax) {
+        const dim3 grid2(xcd_grid_pair((uint32_t)g.a.n_req, (uint32_t)f.a.H));
+        if (qkv_bf16) fused128x2_t<uint16_t>(op, g, grid2, st);
+        else fused128x2_t<float>(op, g, grid2, st);
+    } else if (n_blocks >= kWideTilesMin) {
         fused128<256, 8>(op, qkv_bf16, g, grid, st);
-    else
+    } else {
         fused128<128, 5>(op, qkv_bf16, g, grid, st);
+    }
     return hipGetLastError();
 }
 

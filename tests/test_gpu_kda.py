@@ -116,8 +116,12 @@ def test_kda_mid_size_launch(sq, orc):
     run_teacher_forced(KdaCase(sq, orc, w), w.steps, "kda-mid")
 
 
-def test_kda_head_groups_of_unequal_size(sq, orc):
-    """The per-channel gate over 3 x 100 heads (XCD head groups of 12 and 13)."""
-    w = I.Workload("kh100", 3, 100, 128, 128, 2, {4: 30, 6: 30, 8: 30, 16: 4, 32: 3, I.BITS_BF16: 3},
-                   seed=100)
-    run_teacher_forced(KdaCase(sq, orc, w, n_slots=4, slots=[2, 0, 3]), w.steps, "kda-h100")
+@pytest.mark.parametrize("n_req", [3, 167])
+def test_kda_head_groups_of_unequal_size(sq, orc, n_req):
+    """The per-channel gate over n_req x 100 heads (XCD head groups of 12 and
+    13); 167 requests (16,700 tiles) take the two-tiles-per-workgroup launch."""
+    w = I.Workload(f"kh100x{n_req}", n_req, 100, 128, 128, 2,
+                   {4: 30, 6: 30, 8: 30, 16: 4, 32: 3, I.BITS_BF16: 3}, seed=100 + n_req)
+    slots = list(range(n_req + 1))[::-1][:n_req]
+    run_teacher_forced(KdaCase(sq, orc, w, n_slots=n_req + 1, slots=slots), w.steps,
+                       f"kda-h100x{n_req}")
