@@ -115,36 +115,66 @@ def weighted_error(S: torch.Tensor, infl: torch.Tensor, r: torch.Tensor, c: torc
     return J
 
 
+def column_step(S: torch.Tensor, infl: torch.Tensor, r: torch.Tensor, c: torch.Tensor, bits):
+    """One column update of the fit: with the codes q of the current factors
+    held fixed, c_j minimises sum_states sum_i infl_i (S_ij - r_i c_j q_ij)^2,
+    i.e. c_j = sum infl_i r_i q_ij S_ij / sum infl_i r_i^2 q_ij^2 (a column
+    whose codes are all zero, or whose solution is not positive, keeps its
+    factor).  Heads wider than 8 bits are left alone."""
+    bits = np.asarray(bits)
+    c2 = c.clone()
+    for b in sorted(set(int(x) for x in bits)):
+        if b > 8:
+            continue
+        hs = torch.from_numpy(np.nonzero(bits == b)[0]).to(S.device)
+        Sh, rh, ch = S[:, hs].double(), r[hs].double(), c[hs].double()
+        q = _codes(Sh, (rh[:, :, None] * ch[:, None, :])[None], 2 ** (b - 1) - 1)
+        wi = infl[hs].double()[None, :, :, None]
+        X = rh[None, :, :, None] * q                      # the regressor of c_j
+        num = (wi * X * Sh).sum(dim=(0, 2))
+        den = (wi * X * X).sum(dim=(0, 2))
+        new = torch.where(den > 0, num / den.clamp_min(1e-300), ch)
+        c2[hs] = torch.where(new > 0, new, ch).float()
+    return c2
+
+
+def row_step(S: torch.Tensor, infl: torch.Tensor, r: torch.Tensor, c: torch.Tensor, bits):
+    """One row update: codes fixed, r_i minimises sum_states sum_j
+    infl_i (S_ij - r_i c_j q_ij)^2 -- infl_i is one weight for the whole row,
+    so r_i = sum c_j q_ij S_ij / sum c_j^2 q_ij^2 (same keep rules as
+    column_step)."""
+    bits = np.asarray(bits)
+    r2 = r.clone()
+    for b in sorted(set(int(x) for x in bits)):
+        if b > 8:
+            continue
+        hs = torch.from_numpy(np.nonzero(bits == b)[0]).to(S.device)
+        Sh, rh, ch = S[:, hs].double(), r[hs].double(), c[hs].double()
+        q = _codes(Sh, (rh[:, :, None] * ch[:, None, :])[None], 2 ** (b - 1) - 1)
+        X = ch[None, :, None, :] * q                      # the regressor of r_i
+        num = (X * Sh).sum(dim=(0, 3))
+        den = (X * X).sum(dim=(0, 3))
+        new = torch.where(den > 0, num / den.clamp_min(1e-300), rh)
+        r2[hs] = torch.where(new > 0, new, rh).float()
+    return r2
+
+
 def fit_scales(S: torch.Tensor, infl: torch.Tensor, bits, iters: int = 4):
-    """Key-row-aware dual-axis fit (see the module docstring).  Returns
-    (r, c, history) with history[k] = J per head after iteration k (k = 0 is
-    the max-abs fit)."""
+    """Key-row-aware dual-axis fit (see the module docstring): from the
+    max-abs factors, alternate column_step and row_step, keeping each update
+    only where the head's weighted error J drops.  Returns (r, c, history)
+    with history[k] = J per head after iteration k (k = 0 is the max-abs
+    fit)."""
     bits = np.asarray(bits)
     r, c = maxabs_scales(S, bits)
     J = weighted_error(S, infl, r, c, bits)
     hist = [J.clone()]
     for _ in range(iters):
         for axis in ("col", "row"):
-            r2, c2 = r.clone(), c.clone()
-            for b in sorted(set(int(x) for x in bits)):
-                if b > 8:
-                    continue
-                Q = 2 ** (b - 1) - 1
-                hs = torch.from_numpy(np.nonzero(bits == b)[0]).to(S.device)
-                Sh = S[:, hs].double()
-                rh, ch = r[hs].double(), c[hs].double()
-                q = _codes(Sh, (rh[:, :, None] * ch[:, None, :])[None], Q)
-                wi = infl[hs].double()[None, :, :, None]
-                if axis == "col":
-                    num = (wi * rh[None, :, :, None] * q * Sh).sum(dim=(0, 2))
-                    den = (wi * (rh[None, :, :, None] * q) ** 2).sum(dim=(0, 2))
-                    new = torch.where(den > 0, num / den.clamp_min(1e-300), ch)
-                    c2[hs] = torch.where(new > 0, new, ch).float()
-                else:
-                    num = (ch[None, :, None, :] * q * Sh).sum(dim=(0, 3))
-                    den = ((ch[None, :, None, :] * q) ** 2).sum(dim=(0, 3))
-                    new = torch.where(den > 0, num / den.clamp_min(1e-300), rh)
-                    r2[hs] = torch.where(new > 0, new, rh).float()
+            if axis == "col":
+                r2, c2 = r, column_step(S, infl, r, c, bits)
+            else:
+                r2, c2 = row_step(S, infl, r, c, bits), c
             J2 = weighted_error(S, infl, r2, c2, bits)
             keep = (J2 < J)
             r = torch.where(keep[:, None], r2, r)
@@ -246,6 +276,10 @@ def calibrate(w: I.Workload, budget_mean_bits: float, n_pivots: int, steps: int 
         r, c, hist = fit_scales(S, infl, bb, iters)
         fits[b] = (r, c)
         D[:, i] = hist[-1].cpu().numpy()
+    D_maxabs = np.zeros((H, 3))
+    for i, b in enumerate(WIDTHS):
+        D_maxabs[:, i] = weighted_error(S, infl, *maxabs_scales(S, np.full(H, b)),
+                                        np.full(H, b)).cpu().numpy()
     n_quant = H - n_pivots
     bits = allocate(L.cpu().numpy(), D, int(round(budget_mean_bits * n_quant)), n_pivots)
     r = torch.ones(H, w.dk, device=device)
@@ -258,4 +292,7 @@ def calibrate(w: I.Workload, budget_mean_bits: float, n_pivots: int, steps: int 
             "report": {"mean_bits_nonpivot": float(np.mean(bits[bits <= 8])),
                        "counts": {str(int(b)): int((bits == b).sum()) for b in sorted(set(bits))},
                        "weighted_distortion": float((L.cpu().numpy() *
-                                                     np.where(bits[:, None] == np.array(WIDTHS)[None], D, 0).sum(1)).sum())}}
+                                                     np.where(bits[:, None] == np.array(WIDTHS)[None], D, 0).sum(1)).sum()),
+                       # the same widths with the max-abs factors the fit starts from
+                       "weighted_distortion_maxabs": float((L.cpu().numpy() *
+                                                            np.where(bits[:, None] == np.array(WIDTHS)[None], D_maxabs, 0).sum(1)).sum())}}

@@ -83,22 +83,97 @@ def test_fit_starts_at_maxabs_and_never_worsens():
         assert float((S[:, h].abs() / s0[h]).max()) <= (2 ** (int(b) - 1) - 1) * (1 + 1e-6)
 
 
-def test_column_update_solves_weighted_normal_equations():
-    """With codes fixed, the column step is the WLS solution: residual
-    orthogonal to the weighted regressor."""
-    S = _states(2, N=4, H=1)
-    bits = np.array([6])
-    infl = torch.rand(1, 16, generator=torch.Generator().manual_seed(3)) + 0.1
+def _codes_of(S, r, c, b):
+    s = (r.double()[:, :, None] * c.double()[:, None, :])[None]
+    return torch.clamp(torch.round(S.double() / s), -(2 ** (b - 1) - 1), 2 ** (b - 1) - 1)
+
+
+@pytest.mark.parametrize("b", [4, 6, 8])
+def test_column_step_solves_the_weighted_normal_equations(b):
+    """C.column_step itself: with the codes of the factors it starts from,
+    every column's residual is orthogonal to its influence-weighted regressor
+    r_i q_ij (the stationarity condition of the weighted least squares)."""
+    S = _states(2, N=4, H=2)
+    bits = np.array([b, b])
+    infl = torch.rand(2, 16, generator=torch.Generator().manual_seed(3)) + 0.1
     r, c = C.maxabs_scales(S, bits)
-    Q = 31
-    q = C._codes(S.double(), (r.double()[:, :, None] * c.double()[:, None, :])[None], Q)
-    wi = infl.double()[None, :, :, None]
+    c1 = C.column_step(S, infl, r, c, bits)
+    q = _codes_of(S, r, c, b)
     X = r.double()[None, :, :, None] * q
-    num = (wi * X * S.double()).sum(dim=(0, 2))
-    den = (wi * X * X).sum(dim=(0, 2))
-    cj = num / den
-    resid = S.double() - cj[None, :, None, :] * X
-    assert torch.allclose((wi * X * resid).sum(dim=(0, 2)), torch.zeros_like(cj), atol=1e-9)
+    resid = S.double() - c1.double()[None, :, None, :] * X
+    g = (infl.double()[None, :, :, None] * X * resid).sum(dim=(0, 2))
+    scale = (infl.double()[None, :, :, None] * X.abs() * S.double().abs()).sum(dim=(0, 2))
+    assert torch.all(g.abs() <= 1e-6 * scale), float((g.abs() / scale).max())
+    assert not torch.equal(c1, c)  # the step moved the factors
+
+
+@pytest.mark.parametrize("b", [4, 6, 8])
+def test_row_step_solves_the_per_row_normal_equations(b):
+    """C.row_step itself: each row's residual is orthogonal to c_j q_ij; the
+    row's influence is one weight for the whole row and drops out."""
+    S = _states(4, N=4, H=2)
+    bits = np.array([b, b])
+    infl = torch.rand(2, 16, generator=torch.Generator().manual_seed(5)) + 0.1
+    r, c = C.maxabs_scales(S, bits)
+    r1 = C.row_step(S, infl, r, c, bits)
+    q = _codes_of(S, r, c, b)
+    X = c.double()[None, :, None, :] * q
+    resid = S.double() - r1.double()[None, :, :, None] * X
+    g = (X * resid).sum(dim=(0, 3))
+    scale = (X.abs() * S.double().abs()).sum(dim=(0, 3))
+    assert torch.all(g.abs() <= 1e-6 * scale), float((g.abs() / scale).max())
+    # the row weights do not enter: any other influence gives the same rows
+    assert torch.equal(r1, C.row_step(S, infl * torch.rand(2, 16) + 0.5, r, c, bits))
+
+
+@pytest.mark.parametrize("b", [4, 6, 8])
+def test_steps_recover_planted_factors(b):
+    """States built exactly as r*_i c*_j q_ij: from factors off by a fraction
+    of a step (the same codes), column_step returns c* and row_step r*."""
+    g = torch.Generator().manual_seed(7 + b)
+    Q = 2 ** (b - 1) - 1
+    H, d, N = 2, 16, 3
+    q = torch.randint(-Q, Q + 1, (N, H, d, d), generator=g).double()
+    r_true = (torch.rand(H, d, generator=g) + 0.5).double()
+    c_true = (torch.rand(H, d, generator=g) * 0.1 + 0.01).double()
+    S = (r_true[None, :, :, None] * c_true[None, :, None, :] * q).float()
+    bits = np.array([b] * H)
+    infl = torch.rand(H, d, generator=g) + 0.1
+    delta = 0.2 / Q  # |q| delta < 0.5: the codes do not change
+    c_off = (c_true * (1 + delta)).float()
+    r_off = (r_true * (1 - delta)).float()
+    assert torch.equal(_codes_of(S, r_true.float(), c_off, b), q)
+    c1 = C.column_step(S, infl, r_true.float(), c_off, bits)
+    assert torch.allclose(c1.double(), c_true, rtol=2e-6)
+    r1 = C.row_step(S, infl, r_off, c_true.float(), bits)
+    assert torch.allclose(r1.double(), r_true, rtol=2e-6)
+
+
+def test_uniform_influence_and_exact_states_keep_maxabs():
+    """The fit's two fixed points with uniform influence: (1) a state the
+    max-abs factors represent exactly (J = 0) is left at max-abs, (2) scaling
+    every influence by one constant changes neither the factors nor the keep
+    decisions.  (With uniform influence the fit is a plain least-squares fit,
+    so in general it does not reduce to max-abs: clipping a few outlier
+    codes lowers the squared error.)"""
+    g = torch.Generator().manual_seed(11)
+    bits = np.array([4, 6, 8])
+    S = torch.zeros(3, 3, 8, 8)
+    for h, b in enumerate(bits):
+        Q = 2 ** (int(b) - 1) - 1
+        q = torch.randint(-Q, Q + 1, (3, 8, 8), generator=g).float()
+        q[0, :, 0] = Q  # every row and column reaches +Q somewhere
+        q[0, 0, :] = Q
+        S[:, h] = q * 0.25  # multiples of 0.25; the max-abs step is 0.25 (J = 0 below)
+    uni = torch.ones(3, 8)
+    r0, c0 = C.maxabs_scales(S, bits)
+    assert torch.all(C.weighted_error(S, uni, r0, c0, bits) == 0)
+    r, c, hist = C.fit_scales(S, uni, bits, iters=3)
+    assert torch.equal(r, r0) and torch.equal(c, c0) and all(torch.all(h == 0) for h in hist)
+    S2 = _states(9, N=3, H=3)
+    ra, ca, _ = C.fit_scales(S2, 2.0 * torch.ones(3, 16), bits, iters=3)
+    rb, cb, _ = C.fit_scales(S2, 0.5 * torch.ones(3, 16), bits, iters=3)
+    assert torch.allclose(ra, rb, rtol=1e-6) and torch.allclose(ca, cb, rtol=1e-6)
 
 
 def _fp32_tile(orc, S):
