@@ -57,9 +57,22 @@ def algorithmic_bytes_per_step(w, bits) -> int:
     return state + io
 
 
-# rocprofv3 kernel names of the two timed step instances (bf16 q/k/v)
-STEP_KERNEL = "k_step128<unsigned short, true, false, 128, 5>"
-KDA_KERNEL = "k_step128<unsigned short, true, true, 128, 5>"
+# rocprofv3 kernel names of the two timed step instances (bf16 q/k/v; launches
+# of 16,384 tiles or more, two tiles per workgroup)
+STEP_KERNEL = "k_step128x2<unsigned short, true, false, 5>"
+KDA_KERNEL = "k_step128x2<unsigned short, true, true, 5>"
+
+
+def step_kernel(n_tiles: int, kda: bool = False) -> str:
+    """The d = 128 step instance a launch of n_tiles 4/6/8/16-bit tiles takes
+    (bf16 q/k/v): two tiles per workgroup from 16,384 tiles, four waves per
+    tile from 1,024, else two."""
+    g = "true" if kda else "false"
+    if n_tiles >= 16384:
+        return f"k_step128x2<unsigned short, true, {g}, 5>"
+    if n_tiles >= 1024:
+        return f"k_step128<unsigned short, true, {g}, 256, 8>"
+    return f"k_step128<unsigned short, true, {g}, 128, 5>"
 
 
 def traffic_from_profile(sha: str, workload: str, which: str = "step"):
@@ -246,7 +259,7 @@ def channel_gate_step(sq, I, w, bits, pool, slots, dev, stream, n_in, quant_ms, 
             "traffic": traffic_from_profile(kernel_source_sha(), w.name, "channel_gate_step"),
             "ms_per_step": ms, "hbm_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": byts, "time_vs_scalar_gate_step": ms / quant_ms,
-            "kernel": "k_step128 per-channel-gate instance"}
+            "kernel": step_kernel(w.n_req * w.n_heads, kda=True)}
 
 
 def saturation(sq, w, bits, pool, state):
@@ -607,7 +620,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": "k_step128 (one launch = one decode step over all tiles)",
+            "kernel": step_kernel(w.n_req * w.n_heads) + " (one launch = one decode step over all tiles)",
             "algorithmic_bytes_per_launch": bpstep,
             "avg_launch_ms": ms_per_step,
             "launch_ms_min_median_max": [per[0], per[len(per) // 2], per[-1]],
