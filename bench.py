@@ -170,6 +170,37 @@ def pmc_summary(read_csv: str, write_csv: str, workload: str) -> int:
     return 0
 
 
+CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU",
+                  "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")
+N_XCDS, N_SES, N_SIMDS = 8, 32, 256 * 4
+
+
+def clock_summary(csv_path: str, kernel: str = STEP_KERNEL) -> int:
+    """Per dispatch of `kernel` in a rocprofv3 --pmc run of CLOCK_COUNTERS:
+    duration; counted clock rates (GRBM_GUI_ACTIVE is summed over the 8 XCDs,
+    SQ_CYCLES over the 32 shader engines); VALU wave-instructions issued; and
+    those per SIMD per 4 counted cycles (a wave64 VALU instruction occupies a
+    16-lane SIMD for 4 cycles)."""
+    import csv
+    by = {}
+    for r in csv.DictReader(open(csv_path)):
+        if kernel not in r["Kernel_Name"] or r["Counter_Name"] not in CLOCK_COUNTERS:
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]),
+                          {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    print("| launch | µs | GRBM_GUI_ACTIVE per XCD per µs | SQ_CYCLES per SE per µs | "
+          "VALU wave-instructions | VALU per SIMD per 4 counted cycles |")
+    print("|---|---|---|---|---|---|")
+    for i, (_, d) in enumerate(sorted(by.items())):
+        us = d["ns"] / 1e3
+        cyc = d["SQ_CYCLES"] / N_SES
+        share = d["SQ_INSTS_VALU"] * 4 / (N_SIMDS * cyc) if cyc else float("nan")
+        print(f"| {i + 1} | {us:.1f} | {d['GRBM_GUI_ACTIVE'] / N_XCDS / us:.0f} | {cyc / us:.0f} | "
+              f"{d['SQ_INSTS_VALU']:.4g} | {share:.2f} |")
+    return 0
+
+
 def trace_summary(stats_csv: str) -> int:
     import csv
     for r in csv.DictReader(open(stats_csv)):
@@ -500,6 +531,10 @@ def main() -> int:
                     help="summarise two rocprofv3 --pmc runs of `bench.py --copy-calibration` "
                          "(the read-request and the write-request counters, by size) into "
                          "profiles/ and exit")
+    ap.add_argument("--clock-summary", metavar="PMC_CSV",
+                    help="per-launch clock and VALU table from a rocprofv3 --pmc run of "
+                         "GRBM_GUI_ACTIVE SQ_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU "
+                         "SQ_WAVE_CYCLES, and exit")
     ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
                     help="print the step kernel's row of a rocprofv3 --stats csv and exit")
     args = ap.parse_args()
@@ -507,6 +542,8 @@ def main() -> int:
         return pmc_summary(*args.pmc_summary, args.workload)
     if args.trace_summary:
         return trace_summary(args.trace_summary)
+    if args.clock_summary:
+        return clock_summary(args.clock_summary)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
