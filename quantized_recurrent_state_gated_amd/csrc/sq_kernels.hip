@@ -699,13 +699,20 @@ constexpr float kBias = BITS == 8 ? 0.0f : 1.0f;
 
 // NaN-propagating three-way extremes (v_maximum3_f32 / v_minimum3_f32): a NaN
 // anywhere makes the result NaN, so that the range check below catches it.
+// Written as single instructions so that a block's 16 values reduce in a
+// chain of exactly 8 (the compiler otherwise rebalances the chain into a
+// tree with operands repeated: 9).
 __device__ __forceinline__ float fmax3(float a, float b, float c)
 {
-    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+    float r;
+    asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 __device__ __forceinline__ float fmin3(float a, float b, float c)
 {
-    return __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c);
+    float r;
+    asm("v_minimum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 // Encode one block whose values z(e) are produced on demand by zf, one output
@@ -730,23 +737,31 @@ __device__ __forceinline__ float encode_block(ZF zf, uint32_t (&d)[fw<BITS>() / 
             x = pk_u8(cl(z1), 1, x);
             x = pk_u8(cl(z2), 2, x);
             d[c] = pk_u8(cl(z3), 3, x);
+            // chain: 1 + 1 for the first column's four values, 2 for each later one
             ext = c == 0 ? fmin3(fmin3(z0, z1, z2), z3, z3) : fmin3(fmin3(ext, z0, z1), z2, z3);
         }
     } else if constexpr (BITS == 4) {
-        // even fields into one dword of bytes, odd fields into another, then
-        // interleave the nibbles and add back the bias of every field
+        // even fields into the bytes of one word, odd fields into another,
+        // then the nibbles interleaved and the bias of every field added
+        // back, both words at once as 64-bit shift-adds (every byte is below
+        // 15 here, so nothing carries across a nibble)
+        uint32_t ev[2] = {0u, 0u}, od[2] = {0u, 0u};
 #pragma unroll
-        for (int w = 0; w < 2; w++) {
-            uint32_t ev = 0u, od = 0u;
+        for (int w = 0; w < 2; w++)
 #pragma unroll
             for (int p = 0; p < 4; p++) {
                 const float ze = zf(8 * w + 2 * p), zo = zf(8 * w + 2 * p + 1);
-                ev = pk_u8(cl(ze), p, ev);
-                od = pk_u8(cl(zo), p, od);
+                ev[w] = pk_u8(cl(ze), p, ev[w]);
+                od[w] = pk_u8(cl(zo), p, od[w]);
                 ext = (w == 0 && p == 0) ? fmax3(ze, zo, zo) : fmax3(ext, ze, zo);
             }
-            d[w] = (ev | (od << 4)) + 0x11111111u;
-        }
+        const u32x2 e = {ev[0], ev[1]}, o = {od[0], od[1]};
+        const uint64_t bias = 0x1111111111111111ull;
+        u32x2 x;
+        asm("v_lshl_add_u64 %0, %1, 4, %2" : "=v"(x) : "v"(o), "v"(e));
+        asm("v_lshl_add_u64 %0, %1, 0, %2" : "=v"(x) : "v"(x), "s"(bias));
+        d[0] = x.x;
+        d[1] = x.y;
     } else {
         // four codes of a column -> four bytes (each < 63) -> one 24-bit group
         // f0 | f1 << 6 | f2 << 12 | f3 << 18, as two byte dot products whose
