@@ -27,7 +27,9 @@ analogue of the pages' half-life / accumulated-error correlation (时间维度).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
+import os
 import sys
 import time
 
@@ -242,6 +244,8 @@ def main(argv=None) -> int:
     brief = {k: v for k, v in rep.items() if k != "curves"}
     brief["command"] = "python -m quantized_recurrent_state_gated_amd.drift " + " ".join(
         argv if argv is not None else sys.argv[1:])
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "sq_kernels.hip"), "rb") as f:
+        brief["kernel_source_sha"] = hashlib.sha256(f.read()).hexdigest()[:16]
     if a.curves:
         with open(a.curves, "w") as f:
             json.dump(rep, f)
