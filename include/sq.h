@@ -60,7 +60,8 @@
  *     SQ_ERR_INVALID, nothing enqueued); sq_pool_free switches to it itself.
  *   - A slot must not appear twice in one slot_ids batch: two workgroups would
  *     update the same tile (undefined result).  The step does not check slot
- *     ids on the device; sq_check_slots does, as a separate call.
+ *     ids on the device; sq_check_slots does, as a separate call, and the
+ *     SQ_CHECK switch below makes every call check them on the host.
  *   - Non-finite inputs (alpha, beta, q, k, v, scales) are a caller error.  The
  *     result is defined on the updated value as the kernel evaluates it: a
  *     NaN quotient S'/s becomes code 0, +-Inf the nearest bound +-Q; FP16,
@@ -77,6 +78,22 @@
  *     product, which takes step sizes near the bottom of the fp32 range.
  *   - d_k and d_v must be multiples of 4 and at most 256; d_k = d_v = 128 takes
  *     the tuned kernels, other shapes a plain one.
+ *
+ * SWITCHES (environment variables, read once per pool by sq_pool_alloc; a
+ * pool keeps what it read)
+ *   SQ_CHECK   set and not "0": every call that takes slot ids (store, load,
+ *              step, per-channel step, readout) first copies the ids to the
+ *              host, synchronizing the caller's stream, and returns
+ *              SQ_ERR_INVALID before any kernel is enqueued if an id is
+ *              outside [0, n_slots) or, for the calls that write the pool
+ *              (store and both steps), appears twice.  A debugging aid: it
+ *              costs a synchronization per call and cannot be used under
+ *              graph capture.
+ *   SQ_KERNEL  unset, empty or "tuned": d_k = d_v = 128 takes the tuned
+ *              kernels.  "generic": every shape takes the plain per-width
+ *              kernels, so that the tuned ones can be checked against a second
+ *              implementation on the same data.  Any other value makes
+ *              sq_pool_alloc return SQ_ERR_INVALID (before any HIP call).
  */
 #ifndef SQ_H
 #define SQ_H
@@ -139,8 +156,9 @@ uint64_t sq_pool_bytes(int32_t n_slots, int32_t n_heads, int32_t d_k, int32_t d_
  * row x column factors ([P5] 空间维度).  On success *out receives a handle to
  * release with sq_pool_free.  Errors: SQ_ERR_INVALID (null desc/out/pointers,
  * n_slots or n_heads < 1, state not 256-byte aligned, scales not 16-byte
- * aligned, state_bytes too small, 0 < scale_slot_stride < n_heads),
- * SQ_ERR_UNSUPPORTED (bits, d_k, d_v), SQ_ERR_NOMEM, SQ_ERR_HIP.
+ * aligned, state_bytes too small, 0 < scale_slot_stride < n_heads, an
+ * SQ_KERNEL value that names no kernel family), SQ_ERR_UNSUPPORTED (bits, d_k,
+ * d_v), SQ_ERR_NOMEM, SQ_ERR_HIP.
  * Synchronous (uploads with a blocking copy). */
 int sq_pool_alloc(const sq_pool_desc *desc, sq_pool **out);
 
@@ -184,7 +202,9 @@ int sq_pool_load(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, fl
  * > n_slots, qkv_dtype not an sq_dtype, misaligned pointer, another device
  * current), SQ_ERR_UNSUPPORTED (n_req * n_heads tiles exceed one launch
  * grid), SQ_ERR_HIP (a launch failed).  Device data (slot values, alpha,
- * beta, q/k/v) is not validated; see sq_check_slots for slot ids. */
+ * beta, q/k/v) is not validated; see sq_check_slots for slot ids, and the
+ * SQ_CHECK switch, under which an id out of range or repeated is
+ * SQ_ERR_INVALID (the load and the readout accept repeated ids). */
 int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const void *q,
                    const void *k, const void *v, int32_t qkv_dtype, const float *alpha,
                    const float *beta, float *o, void *stream);

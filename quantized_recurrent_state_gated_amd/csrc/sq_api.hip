@@ -64,6 +64,25 @@ int layout(int32_t n_heads, int32_t dk, int32_t dv, const uint8_t *head_bits,
     return SQ_OK;
 }
 
+// Debug and kernel-selection switches, read from the environment once per
+// pool at sq_pool_alloc.  Returns SQ_ERR_INVALID for an SQ_KERNEL value that
+// names no kernel family, so that a misspelt switch is not silently ignored.
+int read_switches(bool *check_ids, bool *generic)
+{
+    const char *c = getenv("SQ_CHECK");
+    *check_ids = c && *c && strcmp(c, "0") != 0;
+    const char *k = getenv("SQ_KERNEL");
+    if (!k || !*k || strcmp(k, "tuned") == 0) {
+        *generic = false;
+        return SQ_OK;
+    }
+    if (strcmp(k, "generic") == 0) {
+        *generic = true;
+        return SQ_OK;
+    }
+    return SQ_ERR_INVALID;
+}
+
 }  // namespace
 
 struct sq_pool {
@@ -85,6 +104,8 @@ struct sq_pool {
     int32_t *d_err;           // set by the kernels (bit 0: a non-finite updated value), zeroed at alloc
     int32_t *d_heads[kNumClasses];
     int32_t n_class[kNumClasses];
+    bool check_ids;           // SQ_CHECK at sq_pool_alloc: slot ids are checked on the host per call
+    bool generic;             // SQ_KERNEL=generic at sq_pool_alloc: d = 128 takes the generic kernels
 };
 
 extern "C" {
@@ -128,9 +149,13 @@ static int pool_alloc(const sq_pool_desc *desc, sq_pool **out)
     if (st != SQ_OK) return st;
     if (slab > UINT64_MAX / (uint64_t)d.n_slots || d.state_bytes < slab * (uint64_t)d.n_slots)
         return SQ_ERR_INVALID;
+    bool check_ids = false, generic = false;
+    if (int sw = read_switches(&check_ids, &generic)) return sw;
 
     sq_pool *p = new (std::nothrow) sq_pool();
     if (!p) return SQ_ERR_NOMEM;
+    p->check_ids = check_ids;
+    p->generic = generic;
     p->n_slots = d.n_slots;
     p->n_heads = d.n_heads;
     p->dk = d.d_k;
@@ -239,6 +264,29 @@ static int check_device(const sq_pool *p)
     return cur == p->device ? SQ_OK : SQ_ERR_INVALID;
 }
 
+// SQ_CHECK: copy the batch's slot ids to the host (synchronizing the
+// caller's stream) and reject an id outside [0, n_slots), or, for calls that
+// write the pool, an id that appears twice, before any kernel is enqueued.
+static int host_check_ids(const sq_pool *p, const int32_t *ids, int32_t n, bool writes, void *stream)
+{
+    if (int st = check_device(p)) return st;
+    try {
+        std::vector<int32_t> h((size_t)n);
+        if (hipMemcpyAsync(h.data(), ids, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost,
+                           (hipStream_t)stream) != hipSuccess ||
+            hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+            return SQ_ERR_HIP;
+        std::vector<uint8_t> seen(writes ? (size_t)p->n_slots : 0, 0);
+        for (int32_t id : h) {
+            if (id < 0 || id >= p->n_slots) return SQ_ERR_INVALID;
+            if (writes && seen[(size_t)id]++) return SQ_ERR_INVALID;
+        }
+    } catch (...) {
+        return SQ_ERR_NOMEM;
+    }
+    return SQ_OK;
+}
+
 static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16, int32_t n_req,
                        void *stream)
 {
@@ -255,7 +303,7 @@ static int run_classes(const sq_pool *p, sqk::Op op, sqk::StepArgs a, bool bf16,
     // class, widest tiles first
     static const int order[kNumClasses] = {kClassF32, kClassBF16, 3, 2, 1, 0};
     const bool step_or_read = op == sqk::OP_STEP || op == sqk::OP_STEP_KDA || op == sqk::OP_READOUT;
-    if (step_or_read && p->dk == 128 && p->dv == 128) {
+    if (step_or_read && p->dk == 128 && p->dv == 128 && !p->generic) {
         const uint64_t total = tiles;
         if (p->n_class[kClassF32] + p->n_class[kClassBF16] < p->n_heads) {  // any 4/6/8/16-bit heads
             sqk::FusedArgs f;
@@ -291,6 +339,8 @@ int sq_pool_store(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const f
     if (!pool || n_req < 0) return SQ_ERR_INVALID;
     if (n_req == 0) return SQ_OK;
     if (n_req > pool->n_slots || !slot_ids || !S || !aligned(S, 16)) return SQ_ERR_INVALID;
+    if (pool->check_ids)
+        if (int st = host_check_ids(pool, slot_ids, n_req, true, stream)) return st;
     sqk::StepArgs a = base_args(pool, slot_ids);
     a.S = S;
     return run_classes(pool, sqk::OP_STORE, a, false, n_req, stream);
@@ -302,6 +352,8 @@ int sq_pool_load(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, fl
     if (!pool || n_req < 0) return SQ_ERR_INVALID;
     if (n_req == 0) return SQ_OK;
     if (n_req > pool->n_slots || !slot_ids || !S || !aligned(S, 16)) return SQ_ERR_INVALID;
+    if (pool->check_ids)
+        if (int st = host_check_ids(pool, slot_ids, n_req, false, stream)) return st;
     sqk::StepArgs a = base_args(pool, slot_ids);
     a.S = S;
     return run_classes(pool, sqk::OP_LOAD, a, false, n_req, stream);
@@ -318,6 +370,8 @@ int sq_decode_step(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, const 
         return SQ_ERR_INVALID;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (o && !aligned(o, 16)))
         return SQ_ERR_INVALID;
+    if (pool->check_ids)
+        if (int st = host_check_ids(pool, slot_ids, n_req, true, stream)) return st;
     sqk::StepArgs a = base_args(pool, slot_ids);
     a.q = q;
     a.k = k;
@@ -340,6 +394,8 @@ int sq_decode_step_kda(sq_pool *pool, const int32_t *slot_ids, int32_t n_req, co
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
         (o && !aligned(o, 16)))
         return SQ_ERR_INVALID;
+    if (pool->check_ids)
+        if (int st = host_check_ids(pool, slot_ids, n_req, true, stream)) return st;
     sqk::StepArgs a = base_args(pool, slot_ids);
     a.q = q;
     a.k = k;
@@ -358,6 +414,8 @@ int sq_readout(const sq_pool *pool, const int32_t *slot_ids, int32_t n_req, cons
     if (n_req == 0) return SQ_OK;
     if (n_req > pool->n_slots || !slot_ids || !q || !o || !aligned(q, 16) || !aligned(o, 16))
         return SQ_ERR_INVALID;
+    if (pool->check_ids)
+        if (int st = host_check_ids(pool, slot_ids, n_req, false, stream)) return st;
     sqk::StepArgs a = base_args(pool, slot_ids);
     a.q = q;
     a.o = o;

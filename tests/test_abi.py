@@ -73,6 +73,17 @@ def test_pool_alloc_validates_before_any_hip_call(sq, kw, status):
     assert not h.value
 
 
+@pytest.mark.parametrize("value", ["fast", "GENERIC", "tuned ", "1"])
+def test_unknown_kernel_switch_is_rejected_before_any_hip_call(sq, value, monkeypatch):
+    """SQ_KERNEL names a kernel family; a value that names none fails the
+    allocation (host-side, so it is checked here without a GPU)."""
+    monkeypatch.setenv("SQ_KERNEL", value)
+    desc, keep = _desc(sq)
+    h = ctypes.c_void_p()
+    assert sq._lib.sq_pool_alloc(ctypes.byref(desc), ctypes.byref(h)) == sq.SQ_ERR_INVALID
+    assert not h.value
+
+
 def test_null_handles_and_status_strings(sq):
     assert sq._lib.sq_pool_alloc(None, None) == sq.SQ_ERR_INVALID
     sq._lib.sq_pool_free(None)
