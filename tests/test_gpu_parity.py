@@ -513,6 +513,39 @@ def test_head_groups_of_unequal_size(sq, orc, n_req, H):
     run_teacher_forced(Case(sq, orc, w, n_slots=n_req + 1, slots=slots), w.steps, f"h{H}")
 
 
+BOUNDARY_MIXES = {  # n_req x H = the tile count of the launch; about 1:2:1 + 1.4 % pivots
+    (3, 341): {4: 84, 6: 168, 8: 83, 16: 4, 32: 1, I.BITS_BF16: 1},   # 1,023: 128 threads per tile
+    (2, 512): {4: 126, 6: 252, 8: 126, 16: 6, 32: 1, I.BITS_BF16: 1},  # 1,024: 256 threads per tile
+    (43, 381): {4: 94, 6: 188, 8: 93, 16: 4, 32: 1, I.BITS_BF16: 1},   # 16,383: 256 threads per tile
+    (64, 256): {4: 63, 6: 126, 8: 62, 16: 3, 32: 1, I.BITS_BF16: 1},   # 16,384: two tiles per workgroup
+}
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["scalar_gate", "channel_gate"])
+@pytest.mark.parametrize("shape", list(BOUNDARY_MIXES), ids=lambda s: f"{s[0] * s[1]}_tiles")
+def test_launch_size_boundaries(sq, orc, shape, kda):
+    """One step on each side of the two tile counts where the d = 128 launch
+    changes shape (1,024 and 16,384 tiles), every tile compared with the
+    oracle (whole-pool byte comparison; only differing code tiles unpacked)."""
+    from gpu_harness import compare_pools_fast
+    n_req, H = shape
+    w = I.Workload(f"edge{n_req * H}", n_req, H, 128, 128, 1, BOUNDARY_MIXES[shape], seed=n_req + H)
+    assert sum(BOUNDARY_MIXES[shape].values()) == H
+    case = (KdaCase if kda else Case)(sq, orc, w, n_slots=n_req + 1, slots=list(range(1, n_req + 1)))
+    si = case.inputs(0)
+    pre = case.host()
+    o = case.step(si)
+    post = case.host()
+    ref, o_ref = case.oracle_step(pre, si)
+    tally = Tally()
+    compare_pools_fast(tally, post, ref, case.bits, case.off, case.slab, case.slots, w.dk, w.dv)
+    tally.add_o(o.cpu().numpy(), o_ref)
+    say(f"edge {n_req}x{H} kda={kda}: {tally.summary()}")
+    tally.check()
+    assert tally.tiles == n_req * H
+    assert np.array_equal(post[:case.slab], pre[:case.slab])  # slot 0 is not in the batch
+
+
 @pytest.mark.parametrize("dk,dv", [(12, 20), (64, 128), (256, 32)])
 def test_readout_other_shapes(sq, orc, dk, dv):
     """sq_readout through the any-shape kernel, every width: o = S^T q of the
