@@ -521,15 +521,21 @@ BOUNDARY_MIXES = {  # n_req x H = the tile count of the launch; about 1:2:1 + 1.
 }
 
 
+BOUNDARY_CASES = [(shape, "bf16") for shape in BOUNDARY_MIXES] + [((2, 512), "f32"), ((64, 256), "f32")]
+
+
 @pytest.mark.parametrize("kda", [False, True], ids=["scalar_gate", "channel_gate"])
-@pytest.mark.parametrize("shape", list(BOUNDARY_MIXES), ids=lambda s: f"{s[0] * s[1]}_tiles")
-def test_launch_size_boundaries(sq, orc, shape, kda):
+@pytest.mark.parametrize("shape,qkv", BOUNDARY_CASES, ids=lambda c: f"{c[0] * c[1]}_tiles"
+                         if isinstance(c, tuple) else c)
+def test_launch_size_boundaries(sq, orc, shape, qkv, kda):
     """One step on each side of the two tile counts where the d = 128 launch
     changes shape (1,024 and 16,384 tiles), every tile compared with the
-    oracle (whole-pool byte comparison; only differing code tiles unpacked)."""
+    oracle (whole-pool byte comparison; only differing code tiles unpacked);
+    fp32 q/k/v as well as bf16 for the two larger launch shapes."""
     from gpu_harness import compare_pools_fast
     n_req, H = shape
-    w = I.Workload(f"edge{n_req * H}", n_req, H, 128, 128, 1, BOUNDARY_MIXES[shape], seed=n_req + H)
+    w = I.Workload(f"edge{n_req * H}", n_req, H, 128, 128, 1, BOUNDARY_MIXES[shape], qkv_dtype=qkv,
+                   seed=n_req + H)
     assert sum(BOUNDARY_MIXES[shape].values()) == H
     case = (KdaCase if kda else Case)(sq, orc, w, n_slots=n_req + 1, slots=list(range(1, n_req + 1)))
     si = case.inputs(0)
