@@ -540,6 +540,14 @@ def test_launch_size_boundaries(sq, orc, shape, qkv, kda):
     case = (KdaCase if kda else Case)(sq, orc, w, n_slots=n_req + 1, slots=list(range(1, n_req + 1)))
     si = case.inputs(0)
     pre = case.host()
+    if not kda:  # the readout-only instance of the same launch shape, before the step
+        o_r = torch.empty(n_req, H, w.dv, device="cuda")
+        sq.sq_readout(case.pool, case.slots_d, si.q.cuda(), o_r)
+        t_r = Tally()
+        t_r.add_o(o_r.cpu().numpy(), orc.readout_pool(pre, case.bits, w.dk, w.dv, case.r, case.c,
+                                                      case.slots, host_f32(si.q), n_threads=16))
+        t_r.check()
+        assert np.array_equal(case.host(), pre)
     o = case.step(si)
     post = case.host()
     ref, o_ref = case.oracle_step(pre, si)
