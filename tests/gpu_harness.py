@@ -104,6 +104,14 @@ class Tally:
         if gpu.shape[0] == 0:
             return
         self.tiles += gpu.shape[0]
+        if bits <= 8:
+            # a code tile whose bytes match is counted (every code equal)
+            # without unpacking; only tiles with a differing byte are unpacked
+            same = (gpu == ref).all(axis=1)
+            self.codes += int(same.sum()) * (gpu.shape[1] * 8 // I.field_width(bits))
+            if same.all():
+                return
+            gpu, ref = gpu[~same], ref[~same]
         a, b = unpack_fields(gpu, bits), unpack_fields(ref, bits)
         if bits <= 8:
             d = np.abs(a.astype(np.int16) - b.astype(np.int16))

@@ -44,16 +44,36 @@ class DevicePool:
         torch.cuda.synchronize()
         self.rh, self.ch = self.r.cpu().numpy(), self.c.cpu().numpy()
 
+    def _gather_plan(self, tiles):
+        """Per tile size: the positions in `tiles` and the 256-byte rows of the
+        state that hold those tiles (tiles start on 256-byte boundaries and
+        their sizes are multiples of 256).  Computed once per tile list."""
+        key = tuple(tiles)
+        if getattr(self, "_plan_key", None) == key:
+            return self._plan
+        groups = {}
+        for i, (n, h) in enumerate(tiles):
+            off, nb = self.sq.sq_pool_tile_offset(self.pool, int(n), int(h))
+            assert off % 256 == 0 and nb % 256 == 0
+            groups.setdefault(nb, []).append((i, off // 256))
+        plan = []
+        for nb, lst in groups.items():
+            starts = torch.tensor([r for _, r in lst], dtype=torch.int64, device="cuda")
+            rows = (starts[:, None] + torch.arange(nb // 256, device="cuda")[None, :]).reshape(-1)
+            plan.append(([i for i, _ in lst], rows, nb))
+        self._plan_key, self._plan = key, plan
+        return plan
+
     def tile_bytes(self, tiles):
         """uint8 copies of tiles [(n, h)] (slot n holds request n), gathered on
-        the GPU and copied back in one transfer."""
-        views, sizes = [], []
-        for n, h in tiles:
-            off, nb = self.sq.sq_pool_tile_offset(self.pool, int(n), int(h))
-            views.append(self.state[off:off + nb])
-            sizes.append(nb)
-        flat = torch.cat(views).cpu().numpy()
-        return np.split(flat, np.cumsum(sizes)[:-1])
+        the GPU with one row gather per tile size and copied back."""
+        rows_of_state = self.state.view(-1, 256)
+        out = [None] * len(tiles)
+        for idx, rows, nb in self._gather_plan(tiles):
+            g = rows_of_state.index_select(0, rows).view(len(idx), nb).cpu().numpy()
+            for j, i in enumerate(idx):
+                out[i] = g[j]
+        return out
 
 
 def sample(w, bits, rng, n_random):
